@@ -1,0 +1,52 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and show that some pin catches each one."""
+import numpy as np
+import pytest
+
+from oracle import paged_ref
+from tests import oracle_checks as oc
+
+_orig_attend = paged_ref.attend
+_orig_softmax = paged_ref.softmax_weights
+_orig_append = paged_ref.append_ref
+_orig_cow = paged_ref.cow_ref
+_orig_gather = paged_ref.gather_tokens
+
+
+def _gather_ignoring_table(cache, table_row, length, block_size):
+    j = np.arange(length)
+    return cache[j // block_size, :, j % block_size, :]
+
+
+MUTATIONS = {
+    "offset_off_by_one": ("token_position", lambda j, B: (j // B, (j + 1) % B)),
+    "block_and_offset_swapped": ("token_position", lambda j, B: (j % B, j // B)),
+    "gqa_modulo_map": ("kv_head_of", lambda h, hq, hkv: h % hkv),
+    "causal_excludes_self": ("visible_keys", lambda p: p),
+    "causal_one_too_many": ("visible_keys", lambda p: p + 2),
+    "scale_dropped": ("attend", lambda q, K, V, s: _orig_attend(q, K, V, 1.0)),
+    "scale_squared": ("attend", lambda q, K, V, s: _orig_attend(q, K, V, s * s)),
+    "keys_used_as_values": ("attend", lambda q, K, V, s: _orig_attend(q, K, K, s)),
+    "softmax_unnormalised": ("softmax_weights",
+                             lambda x: np.exp(x - np.max(x, axis=-1, keepdims=True))),
+    "softmax_sign_flipped": ("softmax_weights", lambda x: _orig_softmax(-x)),
+    "softmax_drops_last_key": ("softmax_weights",
+                               lambda x: _orig_softmax(x) * (np.arange(x.shape[-1]) < x.shape[-1] - 1)),
+    "table_ignored": ("gather_tokens", _gather_ignoring_table),
+    "append_v_gets_k": ("append_ref", lambda kc, vc, kn, vn, sm, B=16: _orig_append(kc, vc, kn, kn, sm, B)),
+    "append_skips_last": ("append_ref", lambda kc, vc, kn, vn, sm, B=16:
+                          _orig_append(kc, vc, kn, vn, np.where(np.arange(len(sm)) == len(sm) - 1, -1, sm), B)),
+    "cow_k_only": ("cow_ref", lambda kc, vc, p: (_orig_cow(kc, vc, p)[0], np.array(vc, copy=True))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(paged_ref, attr, fn)
+    failed = []
+    for check in oc.ALL_CHECKS:
+        try:
+            check(paged_ref)
+        except (AssertionError, paged_ref.OracleInputError, IndexError, ValueError):
+            failed.append(check.__name__)
+    assert failed, f"mutation {name} passed every pin"
