@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+The headline `value` is paged-decode KV bandwidth (GB/s of K and V bytes of valid tokens read,
+divided by the decode call time) on the 64-sequence decode batch (lengths U[128, 4096], 32/8
+heads, head_dim 128, bf16 KV).  The same JSON line carries the mixed continuous-batching step
+(KV append of 4288 tokens, eight 512-token prefill chunks over paged prefixes, 192 decodes) as
+tokens/s, the 32 x 32768-token long-context decode, and the beam step (112 copy-on-write block
+copies, tail append, decode of 128 beams), each timed with HIP events on the stream the kernels
+run on.  Inputs are synthetic and already resident in HBM when timing starts.
+
+`--gpus N` with N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_cache_341_amd import checks, ops  # noqa: E402
+from paged_kv_cache_341_amd import workloads as W  # noqa: E402
+
+METRIC = "paged decode KV GB/s (% HBM peak) + mixed-batch tokens/s at 1 MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Per-call HIP-event durations on the current stream (ms): (mean, median, total wall)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    region0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return float(per.mean()), float(np.median(per)), float(region0.elapsed_time(region1))
+
+
+def i32(a):
+    return ops.to_device_index(a, "cuda", torch.int32)
+
+
+def i64(a):
+    return ops.to_device_index(a, "cuda", torch.int64)
+
+
+def kv_bytes(seq_lens, num_kv_heads, head_dim, elem_bytes=2) -> int:
+    return int(np.sum(seq_lens, dtype=np.int64)) * 2 * num_kv_heads * head_dim * elem_bytes
+
+
+def decode_callable(b):
+    msl = int(b.seq_lens.max())
+    checks.check_tables(b.block_tables, b.seq_lens, b.k_cache.shape[0], 16, msl)
+    bt, sl = i32(b.block_tables), i32(b.seq_lens)
+    out = torch.empty_like(b.q)
+    ws_n = ops.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                        16, msl)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        ops.pa_decode(out, b.q, b.k_cache, b.v_cache, bt, sl, msl, b.scale, workspace=ws)
+    return fn
+
+
+def bench_decode(b, steps, warmup, name):
+    fn = decode_callable(b)
+    mean_ms, med_ms, total_ms = time_calls(fn, steps, warmup)
+    nbytes = kv_bytes(b.seq_lens, b.num_kv_heads, b.head_dim)
+    gbps = nbytes / (mean_ms * 1e-3) / 1e9
+    log(f"{name}: {mean_ms * 1e3:.1f} us/call (median {med_ms * 1e3:.1f}), "
+        f"{nbytes / 1e6:.1f} MB KV -> {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of HBM)")
+    return dict(ms=mean_ms, median_ms=med_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps)
+
+
+def chunk_flops(prefixes, chunk_lens, num_q_heads, head_dim) -> float:
+    """Causal-pair flops: 4 * D * Hq * sum_c (n_c * P_c + n_c (n_c + 1) / 2)."""
+    tot = 0
+    for p, n in zip(prefixes, chunk_lens):
+        tot += n * int(p) + n * (n + 1) // 2
+    return 4.0 * head_dim * num_q_heads * tot
+
+
+def bench_mixed(steps, warmup):
+    m = W.mixed_bf16(device="cuda", poison=False)
+    nb = m.k_cache.shape[0]
+    checks.check_slots(m.slot_mapping, nb, 16)
+    sm = i64(m.slot_mapping)
+    msl_c = int(m.chunk_seq_lens.max())
+    max_q = int(np.diff(m.query_start_loc).max())
+    checks.check_tables(m.chunk_tables, m.chunk_seq_lens, nb, 16, msl_c)
+    checks.check_chunks(m.query_start_loc, m.chunk_seq_lens, m.q_chunk.shape[0], max_q)
+    ct, cl, qsl = i32(m.chunk_tables), i32(m.chunk_seq_lens), i32(m.query_start_loc)
+    cout = torch.empty_like(m.q_chunk)
+    dec = W.DecodeBatch(q=m.q_decode, k_cache=m.k_cache, v_cache=m.v_cache,
+                        block_tables=m.decode_tables, seq_lens=m.decode_seq_lens, scale=m.scale,
+                        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                        dtype="bf16")
+    dfn = decode_callable(dec)
+
+    def append():
+        ops.kv_append(m.k_cache, m.v_cache, m.k_new, m.v_new, sm)
+
+    def prefill():
+        ops.pa_prefill_chunk(cout, m.q_chunk, m.k_cache, m.v_cache, ct, cl, qsl, max_q, msl_c,
+                             m.scale)
+
+    def step():
+        append()
+        prefill()
+        dfn()
+
+    t_step = time_calls(step, steps, warmup)
+    t_app = time_calls(append, steps, warmup)
+    t_pre = time_calls(prefill, steps, warmup)
+    t_dec = time_calls(dfn, steps, warmup)
+    T = len(m.slot_mapping)
+    flops = chunk_flops(m.extra["prefixes"], np.diff(m.query_start_loc), 32, 128)
+    app_bytes = 2 * T * 8 * 128 * 2 * 2          # read + write of K and V rows
+    dec_bytes = kv_bytes(m.decode_seq_lens, 8, 128)
+    tflops = flops / (t_pre[0] * 1e-3) / 1e12
+    res = dict(
+        tokens_per_s=T / (t_step[0] * 1e-3), ms_per_step=t_step[0], new_tokens=T,
+        append_ms=t_app[0], append_gbps=app_bytes / (t_app[0] * 1e-3) / 1e9,
+        prefill_ms=t_pre[0], prefill_gflop=flops / 1e9, prefill_tflops=tflops,
+        prefill_mfma_frac=tflops / BF16_PEAK_TFLOPS,
+        decode_ms=t_dec[0], decode_kv_bytes=dec_bytes,
+        decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9)
+    log(f"mixed step: {t_step[0] * 1e3:.1f} us -> {res['tokens_per_s']:.0f} tok/s | append "
+        f"{t_app[0] * 1e3:.1f} us | prefill {t_pre[0] * 1e3:.1f} us {tflops:.0f} TFLOP/s "
+        f"({100 * res['prefill_mfma_frac']:.1f}% MFMA) | decode {t_dec[0] * 1e3:.1f} us "
+        f"{res['decode_gbps']:.0f} GB/s")
+    return res
+
+
+def bench_beams(steps, warmup):
+    m = W.beams_bf16(device="cuda", poison=False)
+    nb = m.k_cache.shape[0]
+    checks.check_pairs(m.cow_pairs, nb)
+    checks.check_slots(m.slot_mapping, nb, 16)
+    pairs, sm = i64(m.cow_pairs), i64(m.slot_mapping)
+    dec = W.DecodeBatch(q=m.q_decode, k_cache=m.k_cache, v_cache=m.v_cache,
+                        block_tables=m.decode_tables, seq_lens=m.decode_seq_lens, scale=m.scale,
+                        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                        dtype="bf16")
+    dfn = decode_callable(dec)
+
+    def cow():
+        ops.cow_copy_blocks(m.k_cache, m.v_cache, pairs)
+
+    def step():
+        cow()
+        ops.kv_append(m.k_cache, m.v_cache, m.k_new, m.v_new, sm)
+        dfn()
+
+    t_step = time_calls(step, steps, warmup)
+    t_cow = time_calls(cow, steps, warmup)
+    t_dec = time_calls(dfn, steps, warmup)
+    logical = kv_bytes(m.decode_seq_lens, 8, 128)
+    used = np.unique(np.concatenate([m.decode_tables[i, :-(-int(L) // 16)]
+                                     for i, L in enumerate(m.decode_seq_lens)]))
+    unique_bytes = len(used) * 8 * 16 * 128 * 2 * 2
+    cow_bytes = 2 * m.cow_pairs.shape[0] * 8 * 16 * 128 * 2 * 2
+    res = dict(ms_per_step=t_step[0], cow_ms=t_cow[0], cow_pairs=int(m.cow_pairs.shape[0]),
+               cow_gbps=cow_bytes / (t_cow[0] * 1e-3) / 1e9, decode_ms=t_dec[0],
+               decode_logical_gbps=logical / (t_dec[0] * 1e-3) / 1e9,
+               decode_unique_gbps=unique_bytes / (t_dec[0] * 1e-3) / 1e9)
+    log(f"beam step: {t_step[0] * 1e3:.1f} us | cow {t_cow[0] * 1e3:.1f} us | decode "
+        f"{t_dec[0] * 1e3:.1f} us, {res['decode_logical_gbps']:.0f} GB/s logical, "
+        f"{res['decode_unique_gbps']:.0f} GB/s unique")
+    return res
+
+
+def cpu_baseline(seconds: float = 10.0):
+    """The fp64 oracle on the host cores, over as many sequences of the decode batch as fit in
+    `seconds` (same generator, CPU copy of the inputs)."""
+    from oracle import paged_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    b = W.decode_bf16(device="cpu", poison=False)
+    q = b.q.view(torch.int16).numpy().view(np.uint16)
+    kc = b.k_cache.view(torch.int16).numpy().view(np.uint16)
+    vc = b.v_cache.view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    done = []
+    for s in range(b.num_seqs):
+        ref.decode_ref(q, kc, vc, b.block_tables, b.seq_lens, b.scale, "bf16", seqs=[s])
+        done.append(s)
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = kv_bytes(b.seq_lens[done], 8, 128)
+    gbps = nbytes / dt / 1e9
+    log(f"cpu oracle: {len(done)} of {b.num_seqs} sequences in {dt:.1f} s -> {gbps:.3f} GB/s")
+    return {"value": gbps, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {len(done)} of {b.num_seqs} sequences of the decode batch "
+                      f"({nbytes / 1e6:.0f} MB KV), numpy fp64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged path is "
+              "built and measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    ops.load_library()
+    skip = set(filter(None, args.skip.split(",")))
+    steps, warmup = args.steps, args.warmup
+
+    log("workload decode_bf16 (64 seqs, lens U[128,4096], 32/8 heads, D128, bf16)")
+    b = W.decode_bf16(device="cuda", poison=False)
+    dec = bench_decode(b, steps, warmup, "decode_bf16")
+    S, msl = b.num_seqs, int(b.seq_lens.max())
+    bps_ws = ops.pa_decode_workspace_size(S, 32, 8, 128, 16, msl)
+    del b
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if "mixed" not in skip:
+        extra["mixed_batch"] = bench_mixed(max(steps // 2, 5), warmup)
+        torch.cuda.empty_cache()
+    if "long" not in skip:
+        lb = W.long_bf16(device="cuda", poison=False)
+        extra["long_decode"] = bench_decode(lb, max(steps // 5, 5), max(warmup // 2, 2),
+                                            "long_bf16")
+        del lb
+        torch.cuda.empty_cache()
+    if "beams" not in skip:
+        extra["beam_step"] = bench_beams(max(steps // 2, 5), warmup)
+        torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_bf16: 64 sequences, lengths U[128,4096], 32 q / 8 kv "
+                               "heads, head_dim 128, block_size 16, bf16 KV, fp32 accumulate",
+                   "num_seqs": S, "kv_bytes_per_step": dec["kv_bytes"],
+                   "workspace_bytes": bps_ws},
+        "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "pa_decode (split + merge launches)"},
+    }
+    for k, v in extra.items():
+        result[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+    if "mixed_batch" in extra:
+        result["mixed_batch_tokens_per_s"] = round(extra["mixed_batch"]["tokens_per_s"], 1)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * pagedattn.h - C ABI of the paged KV-cache hot path for MI355X (gfx950).
+ *
+ * The operations follow the pages' statement of the problem:
+ *   - KV lives in a pool of equal, fixed-size physical blocks; a sequence's tokens fill its
+ *     logical blocks left to right and a per-sequence block table maps each logical block to a
+ *     physical one, so token j of a sequence sits in physical block table[j / B] at offset
+ *     j % B.  (study-docs "PagedAttention & Continuous Batching", section "Block tables";
+ *     cloudmash "Batching and PagedAttention", section "PagedAttention", steps 1-2.)
+ *   - Attention gathers K and V through that table instead of assuming one contiguous slab.
+ *     (cloudmash "PagedAttention", step 4; llmdeepdive "7.8", section "Concept".)
+ *   - A sequence grows into its current block and takes a fresh one when it fills.
+ *     (study-docs "Block tables".)
+ *   - Forked sequences share blocks; the first write into a shared block copies it.
+ *     (study-docs "Copy-on-write"; cloudmash "Sharing blocks".)
+ *   - A continuous-batching step mixes chunks of long prompts with single-token decodes.
+ *     (cloudmash "Continuous batching"; llmdeepdive "Concept", continuous-batching paragraph.)
+ *
+ * Layout (every entry point):
+ *   k_cache, v_cache : [num_blocks][num_kv_heads][block_size][head_dim], row-major, one tensor
+ *                      per layer.  A (block, kv head) slab is block_size*head_dim contiguous
+ *                      elements.
+ *   q, out           : [rows][num_q_heads][head_dim], row-major.
+ *   Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *   Element type: all of q, out, k_cache, v_cache, k_new, v_new share `dtype`.  Scores,
+ *   softmax and accumulation are fp32; bf16 outputs are rounded to nearest-even once.
+ *   Block tables and lengths are int32, slot mappings and copy pairs int64.
+ *
+ * Ownership: the caller owns every buffer.  Device pointers must be device memory of the
+ * current HIP device; `stream` is a hipStream_t (NULL = the default stream).  The library never
+ * allocates or frees memory, keeps no pointer after returning, and holds no mutable global state,
+ * so calls from several host threads are safe.  Every call only enqueues work on `stream`: no
+ * host synchronisation, no device-to-host copy.
+ *
+ * Errors: host scalars and pointers are checked before anything is enqueued; a failed check
+ * returns a non-zero status, enqueues nothing, and sets a per-thread message readable through
+ * pa_last_error().  Device contents (table entries, lengths, slots) are preconditions, not
+ * checked: table entries read must lie in [0, num_blocks), 1 <= seq_lens[i] <= max_seq_len,
+ * non-negative slots must be distinct and below num_blocks*block_size, copy destinations must be
+ * distinct and never a source.  Violating them is undefined behaviour.  No C++ exception
+ * crosses this interface.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, misalignment, bad ratio */
+  PA_ERR_UNSUPPORTED = 2,        /* a valid request this build has no kernel for */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_DEVICE = 4              /* the HIP runtime reported an error at launch */
+} pa_status;
+
+typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+/*
+ * pa_decode - one query token per sequence attends to all of its seq_lens[s] cached tokens,
+ * gathered through its block table (cloudmash "PagedAttention" step 4; study-docs "Block
+ * tables").  seq_lens count the token appended in the same step, so that token sees itself.
+ *
+ *   out          [num_seqs][num_q_heads][head_dim]   written
+ *   q            [num_seqs][num_q_heads][head_dim]
+ *   block_tables [num_seqs][max_blocks_per_seq] int32 (entries past ceil(len/B) never read)
+ *   seq_lens     [num_seqs] int32
+ *   max_seq_len  host upper bound of seq_lens; sizes the split grid (no device read-back)
+ *   scale        multiplies q.k before the softmax
+ *   workspace    device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL
+ *                when that size is 0); contents need no initialisation
+ *
+ * Supported: head_dim in {64, 128, 256}; block_size 16; num_q_heads/num_kv_heads in
+ * {1, 2, 4, 8}; dtype F32 or BF16.  Pointers 16-byte aligned.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                    pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode needs for these sizes (0 when no split is needed). */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_seq_len);
+
+/*
+ * pa_prefill_chunk - attention for chunks of new prompt tokens over a paged prefix
+ * (cloudmash "Continuous batching": long prompts are processed in chunks across steps).
+ * Chunk c owns packed query rows query_start_loc[c] .. query_start_loc[c+1]-1; its sequence
+ * holds seq_lens[c] tokens after the chunk was appended, so row i of an n-row chunk sits at
+ * position seq_lens[c]-n+i and sees keys 0 .. seq_lens[c]-n+i: the whole prefix, and the chunk
+ * causally.  A one-row chunk is a decode.
+ *
+ *   out, q          [total_q][num_q_heads][head_dim]
+ *   block_tables    [num_chunks][max_blocks_per_seq] int32
+ *   seq_lens        [num_chunks] int32, each >= the chunk's row count
+ *   query_start_loc [num_chunks+1] int32, rising from 0 to total_q
+ *   max_q_len       host upper bound of the rows in one chunk
+ *   max_seq_len     host upper bound of seq_lens
+ *
+ * Supported: dtype BF16 (MFMA bf16 -> fp32), head_dim 128, block_size 16,
+ * num_q_heads/num_kv_heads in {1, 2, 4, 8}.  Needs no workspace.
+ */
+pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_chunks, int32_t total_q,
+                           int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                           pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Bytes of workspace pa_prefill_chunk needs (currently always 0). */
+size_t pa_prefill_workspace_size(int32_t num_chunks, int32_t total_q, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_seq_len);
+
+/*
+ * kv_append - write new tokens' K and V rows into their slots (study-docs "Block tables": a
+ * sequence grows into its current block).  For each t with slot_mapping[t] >= 0:
+ *   k_cache[slot / block_size][:][slot % block_size][:] = k_new[t][:][:]   (same for V)
+ * as an exact bit copy.  Negative slots are padding and are skipped.
+ *
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  [num_tokens] int64, slot = physical_block * block_size + offset
+ *
+ * Supported: head_dim a multiple of 16 bytes' worth of elements, block_size 16 (any positive
+ * block_size is accepted), F32 or BF16.  num_tokens == 0 is a no-op.
+ */
+pa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                    void* stream);
+
+/*
+ * cow_copy_blocks - copy-on-write block copies (study-docs "Copy-on-write": a write into a
+ * shared block first takes a fresh block and copies the old one into it).  For each pair p:
+ *   k_cache[pairs[p][1]] = k_cache[pairs[p][0]]; v_cache[pairs[p][1]] = v_cache[pairs[p][0]]
+ * whole blocks (every kv head, every slot), as exact bit copies.
+ *
+ *   block_pairs  [num_pairs][2] int64 (src, dst); num_pairs == 0 is a no-op
+ */
+pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Per-thread description of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

@@ -1,0 +1,297 @@
+// C ABI of the paged KV-cache library: argument checks, split planning, dispatch.
+// Every check here runs on host scalars and pointers only, before any HIP call, so a rejected
+// call enqueues nothing.  The entry points are declared and documented in include/pagedattn.h.
+#include "pagedattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pa_dtype d) { return d == PA_DTYPE_BF16 ? 2 : 4; }
+
+bool valid_dtype(pa_dtype d) { return d == PA_DTYPE_F32 || d == PA_DTYPE_BF16; }
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+constexpr int kSupportedBlock = 16;
+
+// Blocks per decode split.  Aims for roughly kTargetGroups workgroups when every sequence is as
+// long as max_seq_len, with 16..64 blocks each; the LDS score buffer caps it at 512/G blocks.
+// PA_DECODE_SPLIT_BLOCKS overrides it (tuning aid).
+int plan_blocks_per_split(int num_seqs, int num_kv_heads, int group, int max_seq_len) {
+  const int nblk = (max_seq_len + kSupportedBlock - 1) / kSupportedBlock;
+  static const int env = [] {
+    const char* e = std::getenv("PA_DECODE_SPLIT_BLOCKS");
+    return e ? std::atoi(e) : 0;
+  }();
+  const int cap = 512 / group;
+  int bps;
+  if (env > 0) {
+    bps = env;
+  } else {
+    constexpr long kTargetGroups = 4096;
+    const long want = (static_cast<long>(nblk) * num_seqs * num_kv_heads + kTargetGroups - 1) /
+                      kTargetGroups;
+    bps = 16;
+    while (bps < want && bps < 64) bps *= 2;
+  }
+  bps = std::min(bps, cap);
+  bps = std::max(bps, 1);
+  return std::min(bps, std::max(nblk, 1));
+}
+
+size_t decode_ws_bytes(int num_seqs, int num_q_heads, int head_dim, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * nsplit;
+  const size_t ml = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+  return ml + rows * head_dim * sizeof(float);
+}
+
+pa_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_DEVICE: return "PA_ERR_DEVICE";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_seq_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size != kSupportedBlock || max_seq_len <= 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int g = num_q_heads / num_kv_heads;
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, max_seq_len);
+  const int nblk = (max_seq_len + block_size - 1) / block_size;
+  const int nsplit = (nblk + bps - 1) / bps;
+  return decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len, float scale, pa_dtype dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: null pointer argument");
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: sizes must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: num_q_heads %d not a multiple of "
+                "num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: unknown dtype");
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: max_seq_len %d exceeds table capacity %lld",
+                max_seq_len, static_cast<long long>(max_blocks_per_seq) * block_size);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: q, out and caches must be 16-byte aligned");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: scale is NaN");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (supported: 64, 128, 256)", head_dim);
+  if (block_size != kSupportedBlock)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (supported: 16)", block_size);
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_group(g))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per kv head (supported: 1,2,4,8)",
+                g);
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, max_seq_len);
+  const int nblk = (max_seq_len + block_size - 1) / block_size;
+  const int nsplit = (nblk + bps - 1) / bps;
+  const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_decode: workspace %zu bytes, need %zu",
+                workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: workspace must be 16-byte aligned");
+  if (nsplit > 65535 || num_kv_heads > 65535 || num_seqs > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * nsplit;
+  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             ((rows * 2 * sizeof(float) + 255) & ~size_t(255)))
+                  : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.bps = bps;
+  a.nsplit_max = nsplit;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.bf16 = dtype == PA_DTYPE_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return device_status(pa::launch_decode(a), "pa_decode launch");
+}
+
+size_t pa_prefill_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+
+pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_chunks, int32_t total_q,
+                           int32_t max_q_len, int32_t max_seq_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, float scale,
+                           pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: null pointer argument");
+  if (num_chunks <= 0 || total_q <= 0 || max_q_len <= 0 || max_seq_len <= 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: sizes must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: num_q_heads %d not a multiple of "
+                "num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (max_q_len > total_q || max_q_len > max_seq_len)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: max_q_len exceeds total_q or "
+                "max_seq_len");
+  if (!valid_dtype(dtype))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: unknown dtype");
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: max_seq_len exceeds table capacity");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: buffers must be 16-byte aligned");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: scale is NaN");
+  if (dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: only bf16 is supported");
+  if (head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: head_dim %d (supported: 128)", head_dim);
+  if (block_size != kSupportedBlock)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: block_size %d (supported: 16)",
+                block_size);
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_group(g))
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: %d query heads per kv head "
+                "(supported: 1,2,4,8)", g);
+  if (num_chunks > 65535 || num_kv_heads > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: grid too large");
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.num_chunks = num_chunks;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.stream = static_cast<hipStream_t>(stream);
+  return device_status(pa::launch_prefill(a), "pa_prefill_chunk launch");
+}
+
+pa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                    const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                    void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_append: sizes must be positive (num_tokens >= 0)");
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "kv_append: unknown dtype");
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_append: null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARGUMENT, "kv_append: buffers must be 16-byte aligned");
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "kv_append: head_dim rows must be a multiple of 16 bytes");
+  pa::AppendArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.elem_bytes = elem_bytes(dtype);
+  a.stream = static_cast<hipStream_t>(stream);
+  return device_status(pa::launch_append(a), "kv_append launch");
+}
+
+pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "cow_copy_blocks: sizes must be positive (num_pairs >= 0)");
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "cow_copy_blocks: unknown dtype");
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !block_pairs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "cow_copy_blocks: null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "cow_copy_blocks: caches must be 16-byte aligned");
+  const int64_t block_bytes =
+      static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "cow_copy_blocks: block bytes must be a multiple of 16");
+  pa::CowArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.pairs = block_pairs;
+  a.num_pairs = num_pairs;
+  a.block_bytes = block_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return device_status(pa::launch_cow(a), "cow_copy_blocks launch");
+}
+
+}  // extern "C"

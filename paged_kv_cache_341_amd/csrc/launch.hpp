@@ -1,0 +1,64 @@
+// Host-side launch descriptors shared by the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace pa {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* ws_ml;        // [S][Hq][nsplit_max][2]  (max in log2 units, sum)
+  float* ws_acc;       // [S][Hq][nsplit_max][D]
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq;
+  int bps, nsplit_max;
+  float scale_log2;
+  bool bf16;
+  hipStream_t stream;
+};
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  int num_chunks, total_q, max_q_len, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq;
+  float scale_log2;
+  hipStream_t stream;
+};
+
+struct AppendArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+  int num_tokens, num_kv_heads, head_dim, block_size, elem_bytes;
+  hipStream_t stream;
+};
+
+struct CowArgs {
+  void* k_cache;
+  void* v_cache;
+  const int64_t* pairs;
+  int num_pairs;
+  int64_t block_bytes;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_append(const AppendArgs& a);
+hipError_t launch_cow(const CowArgs& a);
+
+}  // namespace pa

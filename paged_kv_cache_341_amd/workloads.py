@@ -212,16 +212,18 @@ def mixed_bf16(device="cpu", poison: bool = True, seed: int = SEED_BASE + 4,
                num_decode: int = 192, median: float = 2000.0, sigma: float = 1.0,
                cap: int = 16384, num_q_heads: int = 32, num_kv_heads: int = 8,
                head_dim: int = 128, dtype: str = "bf16",
-               chunk_lens: Optional[Sequence[int]] = None) -> MixedStep:
+               chunk_lens: Optional[Sequence[int]] = None,
+               prefixes: Optional[Sequence[int]] = None) -> MixedStep:
     """Workload 4: chunked prefills over resident prefixes plus single-token decodes.
 
     Before the step, chunk c holds ``prefix[c]`` tokens and decode sequence d holds
     ``L[d] - 1``.  The step appends ``chunk_len`` tokens to each chunk and one to each decode,
     all through one slot mapping ordered chunks first, then decodes.  ``chunk_lens`` overrides
-    the per-chunk query count (ragged chunks).
+    the per-chunk query count (ragged chunks) and ``prefixes`` the resident prefix lengths.
     """
     rng = np.random.default_rng(seed)
-    prefixes = rng.integers(0, max_prefix + 1, size=num_chunks)
+    drawn = rng.integers(0, max_prefix + 1, size=num_chunks)
+    prefixes = drawn if prefixes is None else np.asarray(prefixes, dtype=np.int64)
     dec = np.rint(np.exp(rng.normal(math.log(median), sigma, size=num_decode)))
     dec = np.clip(dec, 1, cap).astype(np.int64)
     clens = [chunk_len] * num_chunks if chunk_lens is None else [int(x) for x in chunk_lens]

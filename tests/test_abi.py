@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad host arguments
+before touching the device (CPU only: no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_341_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH),
+                                reason="libpagedattn.so not built")
+
+INV, UNS, WS = 1, 2, 3
+P = 4096          # a fake, 16-byte aligned, never dereferenced pointer value
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M))
+                  - {"if", "defined"})
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTED), names
+    lib = ctypes.CDLL(ops.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    ops.load_library()
+    assert ops.status_string(0) == "PA_OK"
+    assert ops.status_string(3) == "PA_ERR_WORKSPACE_TOO_SMALL"
+    assert ops.status_string(99) == "PA_ERR_UNKNOWN"
+
+
+def _decode(**kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, sl=P, S=4, Hq=8, Hkv=2, D=128, B=16, NB=64, MB=8,
+             maxlen=100, scale=0.1, dtype=1, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    lib = ops.load_library()
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["S"], a["Hq"],
+                         a["Hkv"], a["D"], a["B"], a["NB"], a["MB"], a["maxlen"], a["scale"],
+                         a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(S=0), INV), (dict(Hq=6, Hkv=4), INV), (dict(maxlen=129), INV),
+    (dict(out=P + 2), INV), (dict(dtype=7), INV), (dict(scale=float("nan")), INV),
+    (dict(D=96), UNS), (dict(B=8, MB=16), UNS), (dict(Hq=32, Hkv=2), UNS),
+    (dict(maxlen=128 * 16, MB=128, S=64, wsb=16), WS),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+    assert ops.load_library().pa_last_error().decode().startswith("pa_decode")
+
+
+def test_decode_workspace_sizes():
+    # one split: no workspace; long sequences: partials for every split
+    assert ops.pa_decode_workspace_size(4, 2, 1, 64, 16, 100) == 0
+    n = ops.pa_decode_workspace_size(32, 16, 4, 256, 16, 32768)
+    assert n > 32 * 16 * 256 * 4
+    assert ops.pa_decode_workspace_size(4, 6, 4, 64, 16, 100) == 0   # invalid ratio
+
+
+def _prefill(**kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, sl=P, qsl=P, C=8, T=4096, maxq=512, maxlen=8704,
+             Hq=32, Hkv=8, D=128, B=16, NB=1000, MB=600, scale=0.1, dtype=1)
+    a.update(kw)
+    lib = ops.load_library()
+    return lib.pa_prefill_chunk(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["qsl"],
+                                a["C"], a["T"], a["maxq"], a["maxlen"], a["Hq"], a["Hkv"], a["D"],
+                                a["B"], a["NB"], a["MB"], a["scale"], a["dtype"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qsl=None), INV), (dict(C=0), INV), (dict(Hq=30), INV), (dict(maxq=5000), INV),
+    (dict(maxlen=600 * 16 + 1), INV), (dict(dtype=0), UNS), (dict(D=64), UNS),
+    (dict(Hq=128, Hkv=8), UNS),
+])
+def test_prefill_rejects(kw, status):
+    assert _prefill(**kw) == status
+
+
+def test_append_and_cow_validation():
+    lib = ops.load_library()
+    # zero tokens / pairs are valid no-ops and touch nothing
+    assert lib.kv_append(None, None, None, None, None, 0, 8, 128, 16, 10, 1, None) == 0
+    assert lib.cow_copy_blocks(None, None, None, 0, 8, 128, 16, 10, 1, None) == 0
+    assert lib.kv_append(P, P, P, None, P, 4, 8, 128, 16, 10, 1, None) == INV
+    assert lib.kv_append(P, P, P, P, P, -1, 8, 128, 16, 10, 1, None) == INV
+    assert lib.kv_append(P, P, P, P, P, 4, 8, 4, 16, 10, 1, None) == UNS   # 8-byte rows
+    assert lib.cow_copy_blocks(P, None, P, 3, 8, 128, 16, 10, 1, None) == INV
+    assert lib.cow_copy_blocks(P, P, P, 3, 8, 128, 16, 10, 5, None) == INV
