@@ -40,24 +40,33 @@ def log(msg: str) -> None:
 
 
 def time_calls(fn, steps: int, warmup: int):
-    """Per-call HIP-event durations on the current stream (ms): (mean, median, total wall)."""
+    """Time `steps` back-to-back calls of fn on the current stream (the stream every binding
+    launches on) with two HIP events around the whole region.  Returns (ms per call, region ms).
+    Per-call event pairs are not used: they would count host launch latency whenever the
+    device drains the queue faster than Python refills it."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
     region0.record(stream)
-    for i in range(steps):
-        starts[i].record(stream)
+    for _ in range(steps):
         fn()
-        ends[i].record(stream)
     region1.record(stream)
     torch.cuda.synchronize()
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    return float(per.mean()), float(np.median(per)), float(region0.elapsed_time(region1))
+    total = float(region0.elapsed_time(region1))
+    return total / steps, total
+
+
+def copy_calibration(mib: int, steps: int = 10) -> None:
+    """A plain device-to-device copy of `mib` MiB, to scale rocprofv3's FETCH_SIZE/WRITE_SIZE
+    (each should read mib * 1024 KiB per dispatch)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms, _ = time_calls(lambda: dst.copy_(src), steps, 2)
+    log(f"copy calibration: {mib} MiB per dispatch ({mib * 1024} KiB read, {mib * 1024} KiB "
+        f"written), {ms * 1e3:.1f} us -> {2 * (mib << 20) / (ms * 1e-3) / 1e9:.0f} GB/s")
 
 
 def i32(a):
@@ -88,12 +97,12 @@ def decode_callable(b):
 
 def bench_decode(b, steps, warmup, name):
     fn = decode_callable(b)
-    mean_ms, med_ms, total_ms = time_calls(fn, steps, warmup)
+    mean_ms, total_ms = time_calls(fn, steps, warmup)
     nbytes = kv_bytes(b.seq_lens, b.num_kv_heads, b.head_dim)
     gbps = nbytes / (mean_ms * 1e-3) / 1e9
-    log(f"{name}: {mean_ms * 1e3:.1f} us/call (median {med_ms * 1e3:.1f}), "
+    log(f"{name}: {mean_ms * 1e3:.1f} us/call, "
         f"{nbytes / 1e6:.1f} MB KV -> {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of HBM)")
-    return dict(ms=mean_ms, median_ms=med_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps)
+    return dict(ms=mean_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps)
 
 
 def chunk_flops(prefixes, chunk_lens, num_q_heads, head_dim) -> float:
@@ -230,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain MIB-MiB device copy (for scaling rocprofv3 counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged path is "
@@ -241,6 +252,8 @@ def main():
     torch.cuda.set_device(0)
     ops.load_library()
     skip = set(filter(None, args.skip.split(",")))
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     steps, warmup = args.steps, args.warmup
 
     log("workload decode_bf16 (64 seqs, lens U[128,4096], 32/8 heads, D128, bf16)")

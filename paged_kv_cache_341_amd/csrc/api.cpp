@@ -147,7 +147,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                 workspace_bytes, need);
   if (need > 0 && !aligned16(workspace))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: workspace must be 16-byte aligned");
-  if (nsplit > 65535 || num_kv_heads > 65535 || num_seqs > 65535)
+  // grid: x = num_seqs * num_kv_heads workgroups of 256 lanes, y = splits
+  if (nsplit > 65535 || static_cast<int64_t>(num_seqs) * num_kv_heads > (int64_t{1} << 24))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
 
   pa::DecodeArgs a{};

@@ -93,9 +93,14 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   __shared__ float stat_m[G];
   __shared__ float stat_l[G];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  // grid.x runs over (sequence, kv head) and grid.y over splits, so consecutive workgroups
+  // belong to different kv heads.  Workgroups are dealt to the 8 XCDs round-robin in launch
+  // order; with this order each XCD gets an even share of every split index (instead of one
+  // XCD holding every sequence's first split), and the beams that share a block read it
+  // through the same XCD's L2.
+  const int kvh = blockIdx.x % num_kv_heads;
+  const int s = blockIdx.x / num_kv_heads;
+  const int split = blockIdx.y;
   const int L = seq_lens[s];
   const int nblk = (L + kBlock - 1) / kBlock;
   const int b_begin = split * bps;
@@ -286,34 +291,72 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   }
 }
 
-// Combine the splits of one (sequence, query head): weights exp2(m_i - M) in split order.
+// Combine the splits of one (sequence, query head) row; one wave per row.  Lanes first read
+// the per-split (max, sum) pairs in parallel, so the split count costs one round trip rather
+// than a chain of dependent loads; then each lane owns D/64 output elements and sums the
+// splits' weighted partial numerators in split order (the same order on every run).
+constexpr int kMergeWaves = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kWave) void pa_decode_merge_kernel(
+__global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
     T* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-    const int32_t* __restrict__ seq_lens, int num_q_heads, int bps, int nsplit_max) {
-  const int s = blockIdx.x / num_q_heads;
+    const int32_t* __restrict__ seq_lens, int num_rows, int num_q_heads, int bps,
+    int nsplit_max) {
+  constexpr int kPer = D / kWave;
+  const int row = blockIdx.x * kMergeWaves + static_cast<int>(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  if (row >= num_rows) return;
+  const int s = row / num_q_heads;
   const int L = seq_lens[s];
   const int nblk = (L + kBlock - 1) / kBlock;
   const int nsplit = (nblk + bps - 1) / bps;
   if (nsplit <= 1) return;
-  const size_t row = blockIdx.x;
-  const float* ml = ws_ml + row * nsplit_max * 2;
+  const float* ml = ws_ml + static_cast<size_t>(row) * nsplit_max * 2;
+  const float* acc = ws_acc + static_cast<size_t>(row) * nsplit_max * D;
+
   float M = kNegInf;
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int i = lane; i < nsplit; i += kWave) M = fmaxf(M, ml[2 * i]);
+  M = group_max<kWave>(M);
   float den = 0.f;
-  for (int i = 0; i < nsplit; ++i) den = fmaf(exp2f(ml[2 * i] - M), ml[2 * i + 1], den);
+  for (int i = lane; i < nsplit; i += kWave) den = fmaf(exp2f(ml[2 * i] - M), ml[2 * i + 1], den);
+  den = group_sum<kWave>(den);
   const float inv = 1.f / den;
-  for (int d = threadIdx.x; d < D; d += kWave) {
-    float num = 0.f;
-    for (int i = 0; i < nsplit; ++i)
-      num = fmaf(exp2f(ml[2 * i] - M), ws_acc[(row * nsplit_max + i) * D + d], num);
-    store_out(out + row * D + d, num * inv);
+
+  float num[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  for (int c = 0; c < nsplit; c += kWave) {
+    const int i = c + lane;
+    const float w = i < nsplit ? exp2f(ml[2 * i] - M) : 0.f;   // this lane's split weight
+    const int cnt = min(kWave, nsplit - c);
+    int k = 0;
+    for (; k + 4 <= cnt; k += 4) {
+      float a[4][kPer];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a[u][e] = acc[static_cast<size_t>(c + k + u) * D + lane + e * kWave];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), k + u));
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) num[e] = fmaf(wu, a[u][e], num[e]);
+      }
+    }
+    for (; k < cnt; ++k) {
+      const float wk = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), k));
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        num[e] = fmaf(wk, acc[static_cast<size_t>(c + k) * D + lane + e * kWave], num[e]);
+    }
   }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_out(out + static_cast<size_t>(row) * D + lane + e * kWave, num[e] * inv);
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a) {
-  const dim3 grid(a.nsplit_max, a.num_kv_heads, a.num_seqs);
+  const dim3 grid(a.num_seqs * a.num_kv_heads, a.nsplit_max);
   const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * kBlock * G,
                                       static_cast<size_t>(kDecodeWaves) * G * D) * sizeof(float);
   hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G>), grid, dim3(kDecodeThreads), lds,
@@ -322,9 +365,11 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
                      static_cast<const T*>(a.v_cache), a.block_tables, a.seq_lens,
                      a.num_kv_heads, a.max_blocks_per_seq, a.bps, a.nsplit_max, a.scale_log2);
   if (a.nsplit_max > 1) {
-    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D>), dim3(a.num_seqs * a.num_kv_heads * G),
-                       dim3(kWave), 0, a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc,
-                       a.seq_lens, a.num_kv_heads * G, a.bps, a.nsplit_max);
+    const int rows = a.num_seqs * a.num_kv_heads * G;
+    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D>),
+                       dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
+                       a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens, rows,
+                       a.num_kv_heads * G, a.bps, a.nsplit_max);
   }
   return hipGetLastError();
 }
