@@ -148,6 +148,17 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
 
+/*
+ * pa_hbm_read_probe - a diagnostic, not part of the paged path: reads `bytes` of device memory
+ * at `src` with 16-byte non-temporal loads (the load the decode kernel streams KV with) on
+ * `num_workgroups` workgroups of 256 lanes, and writes one XOR-folded word per lane to `sink`
+ * (num_workgroups * 256 uint32, device).  Timing it gives the achievable HBM read rate that
+ * decode bandwidth is compared against.  bytes: a positive multiple of 16; src 16-byte aligned;
+ * num_workgroups in [1, 2^20].
+ */
+pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                            int32_t num_workgroups, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* pa_status_string(pa_status s);
 

@@ -295,4 +295,17 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
   return device_status(pa::launch_cow(a), "cow_copy_blocks launch");
 }
 
+pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                            int32_t num_workgroups, void* stream) {
+  if (!src || !sink) return fail(PA_ERR_INVALID_ARGUMENT, "pa_hbm_read_probe: null pointer");
+  if (bytes == 0 || bytes % 16 != 0 || !aligned16(src))
+    return fail(PA_ERR_INVALID_ARGUMENT,
+                "pa_hbm_read_probe: bytes must be a positive multiple of 16, src 16-byte aligned");
+  if (num_workgroups <= 0 || num_workgroups > (1 << 20))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_hbm_read_probe: num_workgroups out of range");
+  return device_status(pa::launch_hbm_probe(src, bytes, sink, num_workgroups,
+                                            static_cast<hipStream_t>(stream)),
+                       "pa_hbm_read_probe launch");
+}
+
 }  // extern "C"

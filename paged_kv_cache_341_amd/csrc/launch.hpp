@@ -60,5 +60,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_append(const AppendArgs& a);
 hipError_t launch_cow(const CowArgs& a);
+hipError_t launch_hbm_probe(const void* src, size_t bytes, uint32_t* sink, int num_workgroups,
+                            hipStream_t stream);
 
 }  // namespace pa

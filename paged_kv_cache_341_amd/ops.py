@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED
 
 EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
-            "pa_last_error")
+            "pa_last_error", "pa_hbm_read_probe")
 
 
 class PagedAttnError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     _vp]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_hbm_read_probe.restype = ctypes.c_int
+    lib.pa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     _lib = lib
@@ -192,6 +194,17 @@ def cow_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: t
     st = lib.cow_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), P, Hkv, D, B, NB,
                              _dtype_code(k_cache), _stream(k_cache, stream))
     _check(st)
+
+
+def pa_hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, num_workgroups: int,
+                      stream=None) -> None:
+    """Stream all of `src` through the read probe; `sink` holds num_workgroups * 256 int32."""
+    lib = load_library()
+    _contig(src, sink)
+    nbytes = src.numel() * src.element_size()
+    _need(sink.numel() * sink.element_size() >= num_workgroups * 256 * 4, "sink too small")
+    _check(lib.pa_hbm_read_probe(_ptr(src), nbytes, _ptr(sink), int(num_workgroups),
+                                 _stream(src, stream)))
 
 
 def status_string(status: int) -> str:

@@ -98,3 +98,12 @@ def test_append_and_cow_validation():
     assert lib.kv_append(P, P, P, P, P, 4, 8, 4, 16, 10, 1, None) == UNS   # 8-byte rows
     assert lib.cow_copy_blocks(P, None, P, 3, 8, 128, 16, 10, 1, None) == INV
     assert lib.cow_copy_blocks(P, P, P, 3, 8, 128, 16, 10, 5, None) == INV
+
+
+def test_read_probe_validation():
+    lib = ops.load_library()
+    assert lib.pa_hbm_read_probe(None, 1024, P, 4, None) == INV
+    assert lib.pa_hbm_read_probe(P, 1000, P, 4, None) == INV        # not a multiple of 16
+    assert lib.pa_hbm_read_probe(P, 0, P, 4, None) == INV
+    assert lib.pa_hbm_read_probe(P + 8, 1024, P, 4, None) == INV    # misaligned
+    assert lib.pa_hbm_read_probe(P, 1024, P, 0, None) == INV
