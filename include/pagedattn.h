@@ -70,7 +70,7 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  *   block_tables [num_seqs][max_blocks_per_seq] int32 (entries past ceil(len/B) never read)
  *   seq_lens     [num_seqs] int32
  *   max_seq_len  host upper bound of seq_lens; sizes the split grid (no device read-back)
- *   scale        multiplies q.k before the softmax
+ *   scale        multiplies q.k before the softmax; finite and > 0
  *   workspace    device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL
  *                when that size is 0); contents need no initialisation
  *
@@ -102,9 +102,11 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *   query_start_loc [num_chunks+1] int32, rising from 0 to total_q
  *   max_q_len       host upper bound of the rows in one chunk
  *   max_seq_len     host upper bound of seq_lens
+ *   scale           multiplies q.k before the softmax; finite and > 0
  *
  * Supported: dtype BF16 (MFMA bf16 -> fp32), head_dim 128, block_size 16,
- * num_q_heads/num_kv_heads in {1, 2, 4, 8}.  Needs no workspace.
+ * num_q_heads/num_kv_heads in {1, 2, 4, 8}.  Needs no workspace.  Up to 128 chunks are
+ * scheduled longest first (ranked on the device from seq_lens); more are taken in order.
  */
 pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* seq_lens,

@@ -129,7 +129,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                 max_seq_len, static_cast<long long>(max_blocks_per_seq) * block_size);
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: q, out and caches must be 16-byte aligned");
-  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: scale is NaN");
+  if (!(scale > 0.f) || scale == __builtin_inff())
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: scale must be finite and positive");
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (supported: 64, 128, 256)", head_dim);
   if (block_size != kSupportedBlock)
@@ -206,7 +207,8 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: max_seq_len exceeds table capacity");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: buffers must be 16-byte aligned");
-  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: scale is NaN");
+  if (!(scale > 0.f) || scale == __builtin_inff())
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: scale must be finite and positive");
   if (dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: only bf16 is supported");
   if (head_dim != 128)
@@ -218,7 +220,9 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (!supported_group(g))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: %d query heads per kv head "
                 "(supported: 1,2,4,8)", g);
-  if (num_chunks > 65535 || num_kv_heads > 65535)
+  // one workgroup of 256 lanes per (chunk, row tile of 128 rows, kv head)
+  const int64_t tiles_max = (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 127) / 128;
+  if (static_cast<int64_t>(num_chunks) * tiles_max * num_kv_heads > (int64_t{1} << 24))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: grid too large");
   pa::PrefillArgs a{};
   a.out = out;

@@ -8,18 +8,30 @@
 //
 // This is a dense contraction, so it runs on MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 // Design (ours):
-//   * Rows of a tile are (token, query head) pairs with the G heads of one kv head innermost, so
-//     the G heads share every K/V tile.  A workgroup owns 128 rows: 4 waves x 32 rows.
-//   * Keys go through LDS 64 at a time (four 16-token blocks, looked up in the table once per
-//     tile).  K is stored row-major with a 16-byte XOR swizzle; V is stored transposed
-//     ([head_dim][key]) with an 8-byte XOR swizzle, because the MFMA operand for P.V needs
-//     consecutive keys of one head-dim column in a lane.
+//   * A work item is (chunk, row tile, kv head).  Rows of a tile are (token, query head) pairs
+//     with the G heads of one kv head innermost, so the G heads share every K/V tile.  A
+//     workgroup owns 128 rows: 4 waves x 32 rows.
+//   * Items are dealt longest chunk first (ranked inside the kernel from seq_lens, no host
+//     read-back), last row tile first within a chunk, kv head fastest.  Workgroups reach the 8
+//     XCDs round-robin in launch order, so with 8 kv heads each XCD serves one head, and the
+//     row tiles of one (chunk, head) read the same prefix through the same L2 at about the
+//     same time.
+//   * Keys go through LDS 64 at a time (four 16-token blocks), double-buffered: the next tile's
+//     K and V are loaded straight into LDS (global_load_lds_dwordx4, one 16-token block per
+//     wave, lanes permuted so rows land XOR-swizzled) while the current tile is computed.  Both
+//     stay row-major ([key][head_dim], as in the pool); the P.V operand, which needs four
+//     consecutive keys of one head-dim column per lane, is read with the gfx950 transposing LDS
+//     load (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of the
+//     8-byte reads of lanes i/4, 4+i/4, 8+i/4, 12+i/4).  One barrier per tile.
 //   * Scores are computed transposed, S^T = K Q^T, so a lane holds one query row: the running
 //     max / sum and the rescale of the output accumulator are per-lane scalars, and the
 //     probabilities are already laid out as the B operand of O^T = V^T P^T.  P is rounded to
-//     bf16 for that product; everything else stays fp32.
-//   * Masking is by selection (-inf scores, zero-filled K/V past the sequence end), applied
-//     only to tiles that reach past a row's position.
+//     bf16 for that product; everything else stays fp32.  The running max is raised only when
+//     a row's new maximum exceeds it by more than 2^8 in probability (probabilities then stay
+//     below 256), so most tiles skip the accumulator rescale.
+//   * Masking is by selection (-inf scores; V zero-filled past the sequence end), applied only
+//     to tiles that reach past a row's position.  K past the end is left as whatever the LDS
+//     buffer held: its scores are always replaced by -inf.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -34,11 +46,26 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kTileRows = kWaves * kRowsPerWave;   // 128
 constexpr int kKvTile = 64;                         // keys per LDS tile (4 blocks)
 constexpr int kChunks = kD / 8;                     // 16-byte chunks per K row
+constexpr int kRankCap = 128;                       // chunks ranked longest-first in-kernel
+constexpr float kLazyLog2 = 8.f;                    // rescale only past 2^8 growth
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// 8-byte-group swizzle of the transposed V tile: row d, key group kg (4 keys).
-__device__ __forceinline__ int vt_group(int d, int kg) { return kg ^ (((d >> 1) ^ (d >> 3)) & 15); }
+// Swizzles of the row-major LDS tiles, in 16-byte chunks of a 256-byte key row.  K rows are
+// read one chunk per lane down 32 keys, V rows eight keys at a time by the transposing load.
+__device__ __forceinline__ int k_swz(int key, int chunk) { return chunk ^ (key & 15); }
+__device__ __forceinline__ int v_swz(int key, int chunk) { return chunk ^ ((key & 3) << 2); }
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Transposing LDS read of 8 bytes (gfx950 ds_read_b64_tr_b16).
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace
 
@@ -47,14 +74,73 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
     bf16_t* __restrict__ out, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_start_loc,
-    int num_kv_heads, int max_blocks_per_seq, float scale_log2) {
+    int num_chunks, int num_kv_heads, int max_blocks_per_seq, int tiles_max, float scale_log2) {
   constexpr int kTokPerTile = kTileRows / G;
-  __shared__ uint4 sK[kKvTile * kChunks];            // 16 KiB
-  __shared__ uint32_t sVT[kD * kKvTile / 2];         // 16 KiB
+  // two buffers per operand, as distinct arrays: the loop is unrolled by two so every access
+  // names its buffer at compile time, which lets the compiler see that the direct-to-LDS loads
+  // into one buffer cannot alias the reads of the other (no wait for the prefetch)
+  __shared__ uint4 sK0[kKvTile * kChunks], sK1[kKvTile * kChunks];        // 2 x 16 KiB
+  __shared__ uint4 sV0[kKvTile * kChunks], sV1[kKvTile * kChunks];        // 2 x 16 KiB
+  __shared__ int s_len[kRankCap];
+  __shared__ int s_scan[kRankCap];
+  __shared__ int s_item[2];
 
-  const int tile = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int c = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int w = blockIdx.x;
+
+  // ------------------------------------------------------------------- which work item
+  int c, tile, kvh;
+  if (num_chunks <= kRankCap) {
+    // rank chunks by length (descending, ties by index), then find item w in that order:
+    // chunk rank r owns tiles(r) * num_kv_heads consecutive items, last row tile first.
+    int my_len = 0, my_items = 0, my_rank = 0;
+    if (tid < num_chunks) {
+      my_len = seq_lens[tid];
+      const int n = query_start_loc[tid + 1] - query_start_loc[tid];
+      my_items = (n * G + kTileRows - 1) / kTileRows * num_kv_heads;
+      s_len[tid] = my_len;
+    }
+    if (tid == 0) s_item[0] = -1;
+    __syncthreads();
+    if (tid < num_chunks) {
+      for (int j = 0; j < num_chunks; ++j) {
+        const int lj = s_len[j];
+        my_rank += (lj > my_len) || (lj == my_len && j < tid);
+      }
+      s_scan[my_rank] = my_items;
+    }
+    __syncthreads();
+    // inclusive scan of the items in rank order
+    for (int off = 1; off < kRankCap; off <<= 1) {
+      int v = 0;
+      if (tid < num_chunks && tid >= off) v = s_scan[tid - off];
+      __syncthreads();
+      if (tid < num_chunks) s_scan[tid] += v;
+      __syncthreads();
+    }
+    if (tid < num_chunks) {
+      const int end = s_scan[my_rank];
+      const int begin = end - my_items;
+      if (w >= begin && w < end) {
+        s_item[0] = tid;
+        s_item[1] = w - begin;
+      }
+    }
+    __syncthreads();
+    c = s_item[0];
+    if (c < 0) return;                                   // past the last item
+    const int local = s_item[1];
+    const int n = query_start_loc[c + 1] - query_start_loc[c];
+    const int tiles = (n * G + kTileRows - 1) / kTileRows;
+    tile = tiles - 1 - local / num_kv_heads;
+    kvh = local % num_kv_heads;
+  } else {
+    c = w / (tiles_max * num_kv_heads);
+    const int rem = w % (tiles_max * num_kv_heads);
+    tile = rem / num_kv_heads;
+    kvh = rem % num_kv_heads;
+  }
+
   const int q0 = query_start_loc[c];
   const int n = query_start_loc[c + 1] - q0;
   const int t_begin = tile * kTokPerTile;
@@ -66,7 +152,6 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
   const int32_t* table = block_tables + static_cast<size_t>(c) * max_blocks_per_seq;
   const size_t slab = static_cast<size_t>(kBlock) * kD;
 
-  const int tid = threadIdx.x;
   const int wave = wave_uniform(tid / kWave);
   const int lane = tid % kWave;
   const int half = lane / 32;        // which 8-wide k slice of an MFMA operand this lane holds
@@ -93,145 +178,169 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
     for (int ks = 0; ks < kD / 16; ++ks) qreg[ks] = load16(qp + ks * 16);
   }
 
+  // ------------------------------------------------------------------ tile staging
+  // Block ids of tile kt's four blocks (wave-uniform scalar loads; 0 past the table's end,
+  // never dereferenced since every load below is guarded by the sequence length).
+  auto tile_phys = [&](int kt, int (&ph)[4]) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int lb = kt * 4 + b;
+      ph[b] = lb < nblk ? wave_uniform(table[lb]) : 0;
+    }
+  };
+  auto pick = [](const int (&ph)[4], int b) {
+    return b == 0 ? ph[0] : b == 1 ? ph[1] : b == 2 ? ph[2] : ph[3];
+  };
+  // K and V: wave w fills block w of the tile (keys 16w .. 16w+15) with four 1 KiB
+  // direct-to-LDS loads each; in load j lane l writes LDS chunk (16w + 4j + l/16, l%16) and so
+  // fetches the logical chunk whose swizzled position that is.  V slots past the sequence end
+  // are zero-filled instead (p = 0 there, and 0 * garbage could be NaN); K slots there are left
+  // alone, since their scores are masked.
+  auto load_kv = [&](int kt, const int (&ph)[4], uint4* kdst, uint4* vdst) {
+    const size_t base = (static_cast<size_t>(pick(ph, wave)) * num_kv_heads + kvh) * slab;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int slot = 4 * j + lane / 16;
+      const int key = wave * kBlock + slot;
+      const int pchunk = lane % 16;
+      uint4* kd = kdst + (wave * kBlock + 4 * j) * kChunks;
+      uint4* vd = vdst + (wave * kBlock + 4 * j) * kChunks;
+      if (kt * kKvTile + key < L) {
+        __builtin_amdgcn_global_load_lds(k_cache + base + slot * kD + k_swz(key, pchunk) * 8, kd,
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(v_cache + base + slot * kD + v_swz(key, pchunk) * 8, vd,
+                                         16, 0, 0);
+      } else {
+        vd[lane] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
   f32x16_t oacc[kD / 32];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-  float m_run = kNegInf;
+  float m_run = kNegInf;     // raw-score units
   float l_run = 0.f;
+  const float lazy_raw = kLazyLog2 / scale_log2;
 
-  for (int kt = 0; kt < num_kv_tiles; ++kt) {
-    // ------------------------------------------------------------- stage K and V^T in LDS
-    __syncthreads();
-    {
-      int phys[4];
+  // one tile: prefetch tile kt+1 into the other buffers, compute tile kt, publish kt+1
+  auto step = [&](int kt, const uint4* kcur, const uint4* vcur, uint4* knext, uint4* vnext) {
+    if (kt + 1 < num_kv_tiles) {
+      int ph[4];
+      tile_phys(kt + 1, ph);
+      load_kv(kt + 1, ph, knext, vnext);
+    }
+
+    if (kt * kKvTile < kv_end_w) {
+      // --------------------------------------------------------------- S^T = K Q^T
+      f32x16_t sacc[2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int lb = kt * 4 + b;
-        phys[b] = lb < nblk ? wave_uniform(table[lb]) : 0;
-      }
-      // K: thread -> (block j, slot tid/16, chunk tid%16); one wave reads 4 whole rows
-      const int slot = tid >> 4;
-      const int ch = tid & 15;
+      for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = j * kBlock + slot;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (kt * kKvTile + key < L) {
-          const bf16_t* kp = k_cache +
-              (static_cast<size_t>(phys[j]) * num_kv_heads + kvh) * slab + slot * kD + ch * 8;
-          val = load16(kp);
-        }
-        sK[key * kChunks + (ch ^ (key & 15))] = val;
-      }
-      // V: thread -> (key pair, chunk); two keys' chunks are interleaved into key-pair words
+        for (int v = 0; v < 16; ++v) sacc[t2][v] = 0.f;
+        const int key = t2 * 32 + col;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int kp2 = (tid >> 4) + 16 * j;      // key pair 0..31
-        const int k0 = 2 * kp2;
-        const int b = k0 >> 4;
-        const int sl = k0 & 15;
-        int pb = phys[0];
-        pb = b == 1 ? phys[1] : pb;
-        pb = b == 2 ? phys[2] : pb;
-        pb = b == 3 ? phys[3] : pb;
-        const bf16_t* vp =
-            v_cache + (static_cast<size_t>(pb) * num_kv_heads + kvh) * slab + sl * kD + ch * 8;
-        const int kabs = kt * kKvTile + k0;
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (kabs < L) v0 = load16(vp);
-        if (kabs + 1 < L) v1 = load16(vp + kD);
-        const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w};
-        const uint32_t bb[4] = {v1.x, v1.y, v1.z, v1.w};
-        const int kg = k0 >> 2;
-        const int wsub = (k0 >> 1) & 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = ch * 8 + e;
-          const uint32_t lo = a[e / 2], hi = bb[e / 2];
-          const uint32_t w = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                     : ((lo & 0xffffu) | (hi << 16));
-          sVT[d * (kKvTile / 2) + vt_group(d, kg) * 2 + wsub] = w;
+        for (int ks = 0; ks < kD / 16; ++ks) {
+          const int chn = ks * 2 + half;
+          const uint4 a = kcur[key * kChunks + k_swz(key, chn)];
+          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]),
+                                                             sacc[t2], 0, 0, 0);
         }
       }
-    }
-    __syncthreads();
-    if (kt * kKvTile >= kv_end_w) continue;     // all keys of this tile are in this wave's future
 
-    // ----------------------------------------------------------------- S^T = K Q^T
-    f32x16_t sacc[2];
+      // --------------------------------------------------------------- online softmax
+      const bool need_mask = kt * kKvTile + kKvTile - 1 > prefix + t_lo_w;
+      if (need_mask) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
+        for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[t2][v] = 0.f;
-      const int key = t2 * 32 + col;
-#pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const int chn = ks * 2 + half;
-        const uint4 a = sK[key * kChunks + (chn ^ (key & 15))];
-        sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]),
-                                                           sacc[t2], 0, 0, 0);
+          for (int v = 0; v < 16; ++v) {
+            const int key = kt * kKvTile + t2 * 32 + (v / 4) * 8 + half * 4 + (v % 4);
+            sacc[t2][v] = key <= pos ? sacc[t2][v] : kNegInf;
+          }
       }
-    }
-
-    // ----------------------------------------------------------------- online softmax
-    const bool need_mask = kt * kKvTile + kKvTile - 1 > prefix + t_lo_w;
-    float x[32];
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float s = sacc[t2][v] * scale_log2;
-        if (need_mask) {
-          const int key = kt * kKvTile + t2 * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-          s = key <= pos ? s : kNegInf;
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[t2][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // raise the running max only when some row of the wave grew past the lazy margin
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy_raw) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      }
+      const float mc = m_run * scale_log2;
+      float psum = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(fmaf(sacc[t2][v], scale_log2, -mc));
+          sacc[t2][v] = p;
+          psum += p;
         }
-        x[t2 * 16 + v] = s;
-      }
-    float mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = exp2f(x[i] - m_new);
-      psum += x[i];
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      l_run += psum;
 
-    // P^T operand for k-step s: the lane's own scores v = (s%2)*8 .. +8 of key subtile s/2
-    uint4 pT[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float* p = x + (s / 2) * 16 + (s % 2) * 8;
-      pT[s] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
-    }
-
-    // ----------------------------------------------------------------- O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) {
-      const int d = dt * 32 + col;
-      const uint32_t* row = sVT + d * (kKvTile / 2);
+      // P^T operand for k-step s: the lane's own scores v = (s%2)*8 .. +8 of key subtile s/2
+      uint4 pT[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int kg0 = 8 * (s / 2) + 4 * (s % 2) + half;
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + vt_group(d, kg0) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + vt_group(d, kg0 + 2) * 2);
-        const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pT[s]),
-                                                           oacc[dt], 0, 0, 0);
+        const f32x16_t& p = sacc[s / 2];
+        const int o = (s % 2) * 8;
+        pT[s] = make_uint4(pack_bf16x2(p[o + 0], p[o + 1]), pack_bf16x2(p[o + 2], p[o + 3]),
+                           pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7]));
+      }
+
+      // --------------------------------------------------------------- O^T += V^T P^T
+      // k-step s covers keys 16s + {0..3, 8..11} + 4*half for this lane's half (the order the
+      // scores sit in); the A operand (d = dt*32 + col, those 8 keys) is two transposing reads,
+      // keys +0..3 and +8..11.  Lane l = 16g + j reads key row (.. + j/4), 8-byte unit
+      // dt*8 + (g%2)*4 + j%4 of it.
+      const int g = lane / 16;
+      const int jj = lane % 16;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const int unit = dt * 8 + (g % 2) * 4 + (jj % 4);     // 8-byte unit of the d range
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint2 part[2];
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const int key = 16 * s + 8 * sub + 4 * half + jj / 4;
+            const char* rowp = reinterpret_cast<const char*>(vcur + key * kChunks);
+            part[sub] = lds_read_tr16(rowp + v_swz(key, unit >> 1) * 16 + (unit & 1) * 8);
+          }
+          const uint4 a = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pT[s]),
+                                                             oacc[dt], 0, 0, 0);
+        }
       }
     }
+
+    __builtin_amdgcn_s_waitcnt(0);    // the direct-to-LDS loads have landed
+    __syncthreads();
+  };
+
+  // prologue: tile 0 into buffers 0
+  {
+    int ph[4];
+    tile_phys(0, ph);
+    load_kv(0, ph, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < num_kv_tiles; kt += 2) {
+    step(kt, sK0, sV0, sK1, sV1);
+    if (kt + 1 < num_kv_tiles) step(kt + 1, sK1, sV1, sK0, sV0);
   }
 
   // ------------------------------------------------------------------------- write out
@@ -244,22 +353,23 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = dt * 32 + g4 * 8 + half * 4;
-        const uint2 w = make_uint2(pack_bf16x2(oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv),
-                                   pack_bf16x2(oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv));
-        *reinterpret_cast<uint2*>(op + d) = w;
+        const uint2 wv =
+            make_uint2(pack_bf16x2(oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv),
+                       pack_bf16x2(oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv));
+        *reinterpret_cast<uint2*>(op + d) = wv;
       }
   }
 }
 
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a) {
-  const int tiles = (a.max_q_len * G + kTileRows - 1) / kTileRows;
-  const dim3 grid(tiles, a.num_kv_heads, a.num_chunks);
-  hipLaunchKernelGGL((pa_prefill_kernel<G>), grid, dim3(kThreads), 0, a.stream,
-                     static_cast<bf16_t*>(a.out), static_cast<const bf16_t*>(a.q),
+  const int tiles_max = (a.max_q_len * G + kTileRows - 1) / kTileRows;
+  const int64_t items = static_cast<int64_t>(a.num_chunks) * tiles_max * a.num_kv_heads;
+  hipLaunchKernelGGL((pa_prefill_kernel<G>), dim3(static_cast<unsigned>(items)), dim3(kThreads),
+                     0, a.stream, static_cast<bf16_t*>(a.out), static_cast<const bf16_t*>(a.q),
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.v_cache),
-                     a.block_tables, a.seq_lens, a.query_start_loc, a.num_kv_heads,
-                     a.max_blocks_per_seq, a.scale_log2);
+                     a.block_tables, a.seq_lens, a.query_start_loc, a.num_chunks,
+                     a.num_kv_heads, a.max_blocks_per_seq, tiles_max, a.scale_log2);
   return hipGetLastError();
 }
 

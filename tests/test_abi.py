@@ -53,6 +53,7 @@ def _decode(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), INV), (dict(S=0), INV), (dict(Hq=6, Hkv=4), INV), (dict(maxlen=129), INV),
     (dict(out=P + 2), INV), (dict(dtype=7), INV), (dict(scale=float("nan")), INV),
+    (dict(scale=0.0), INV), (dict(scale=-0.1), INV), (dict(scale=float("inf")), INV),
     (dict(D=96), UNS), (dict(B=8, MB=16), UNS), (dict(Hq=32, Hkv=2), UNS),
     (dict(maxlen=128 * 16, MB=128, S=64, wsb=16), WS),
 ])
@@ -82,6 +83,7 @@ def _prefill(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(qsl=None), INV), (dict(C=0), INV), (dict(Hq=30), INV), (dict(maxq=5000), INV),
     (dict(maxlen=600 * 16 + 1), INV), (dict(dtype=0), UNS), (dict(D=64), UNS),
+    (dict(scale=-1.0), INV),
     (dict(Hq=128, Hkv=8), UNS),
 ])
 def test_prefill_rejects(kw, status):

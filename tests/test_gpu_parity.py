@@ -147,6 +147,40 @@ def test_prefill_ragged_chunks(G):
     assert_close(widen(out), want, ATOL, RTOL, f"prefill G{G}")
 
 
+def _prefill_case(seed, chunk_lens, prefixes, G, num_kv_heads=2):
+    m = W.mixed_bf16(device=DEV, num_chunks=len(chunk_lens), chunk_len=0, num_decode=1,
+                     median=20, cap=40, num_q_heads=G * num_kv_heads,
+                     num_kv_heads=num_kv_heads, head_dim=128, seed=seed,
+                     chunk_lens=list(chunk_lens), prefixes=list(prefixes))
+    run_append(m.k_cache, m.v_cache, m.k_new, m.v_new, m.slot_mapping)
+    out = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
+                      m.query_start_loc, m.scale)
+    want = ref.prefill_ref(raw(m.q_chunk), raw(m.k_cache), raw(m.v_cache), m.chunk_tables,
+                           m.chunk_seq_lens, m.query_start_loc, m.scale, "bf16")
+    return m, out, want
+
+
+def test_prefill_many_chunks_natural_order():
+    """More chunks than the kernel ranks longest-first: they are scheduled in order."""
+    say("case: prefill 131 small chunks (natural order path)")
+    rng = np.random.default_rng(1500)
+    lens = rng.integers(1, 40, size=131)
+    pre = rng.integers(0, 200, size=131)
+    _, out, want = _prefill_case(1501, lens, pre, G=4)
+    assert_close(widen(out), want, ATOL, RTOL, "prefill 131 chunks")
+
+
+def test_prefill_short_and_tied_chunks():
+    """Sequences shorter than one 64-key tile, and chunks of equal length (rank ties)."""
+    say("case: prefill short sequences and tied lengths, G=8")
+    m, out, want = _prefill_case(1502, [1, 3, 64, 64, 64, 17, 130], [0, 10, 100, 100, 100, 0, 0],
+                                 G=8)
+    assert_close(widen(out), want, ATOL, RTOL, "prefill short/tied")
+    again = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
+                        m.query_start_loc, m.scale)
+    assert torch.equal(again, out), "prefill reruns differ"
+
+
 def test_prefill_one_row_chunk_equals_decode():
     say("case: a one-row chunk is a decode")
     b = W.make_decode([1, 40, 1000, 4095], 8, 2, 128, "bf16", seed=1100, device=DEV)
