@@ -235,19 +235,29 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
 
     if (kt * kKvTile < kv_end_w) {
       // --------------------------------------------------------------- S^T = K Q^T
+      // operands are read a half of the head dim at a time, then the two key subtiles'
+      // MFMAs alternate so back-to-back MFMAs never depend on each other
       f32x16_t sacc[2];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[t2][v] = 0.f;
-        const int key = t2 * 32 + col;
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-          const int chn = ks * 2 + half;
-          const uint4 a = kcur[key * kChunks + k_swz(key, chn)];
-          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]),
-                                                             sacc[t2], 0, 0, 0);
+      for (int kh = 0; kh < 2; ++kh) {
+        uint4 a[2][4];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int key = t2 * 32 + col;
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4)
+            a[t2][k4] = kcur[key * kChunks + k_swz(key, (kh * 4 + k4) * 2 + half)];
         }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2)
+            sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(a[t2][k4]), as_bf16x8(qreg[kh * 4 + k4]), sacc[t2], 0, 0, 0);
       }
 
       // --------------------------------------------------------------- online softmax
@@ -308,10 +318,11 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
       const int g = lane / 16;
       const int jj = lane % 16;
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) {
-        const int unit = dt * 8 + (g % 2) * 4 + (jj % 4);     // 8-byte unit of the d range
+      for (int s = 0; s < 4; ++s) {
+        uint4 a[kD / 32];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int dt = 0; dt < kD / 32; ++dt) {
+          const int unit = dt * 8 + (g % 2) * 4 + (jj % 4);   // 8-byte unit of the d range
           uint2 part[2];
 #pragma unroll
           for (int sub = 0; sub < 2; ++sub) {
@@ -319,10 +330,12 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
             const char* rowp = reinterpret_cast<const char*>(vcur + key * kChunks);
             part[sub] = lds_read_tr16(rowp + v_swz(key, unit >> 1) * 16 + (unit & 1) * 8);
           }
-          const uint4 a = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pT[s]),
-                                                             oacc[dt], 0, 0, 0);
+          a[dt] = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
         }
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[dt]), as_bf16x8(pT[s]),
+                                                             oacc[dt], 0, 0, 0);
       }
     }
 
