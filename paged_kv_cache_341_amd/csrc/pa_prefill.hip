@@ -10,28 +10,30 @@
 // Design (ours):
 //   * A work item is (chunk, row tile, kv head).  Rows of a tile are (token, query head) pairs
 //     with the G heads of one kv head innermost, so the G heads share every K/V tile.  A
-//     workgroup owns 128 rows: 4 waves x 32 rows.
+//     workgroup owns 256 rows: 8 waves x 32 rows, one workgroup per CU (two waves per SIMD).
 //   * Items are dealt longest chunk first (ranked inside the kernel from seq_lens, no host
 //     read-back), last row tile first within a chunk, kv head fastest.  Workgroups reach the 8
 //     XCDs round-robin in launch order, so with 8 kv heads each XCD serves one head, and the
-//     row tiles of one (chunk, head) read the same prefix through the same L2 at about the
-//     same time.
-//   * Keys go through LDS 64 at a time (four 16-token blocks), double-buffered: the next tile's
-//     K and V are loaded straight into LDS (global_load_lds_dwordx4, one 16-token block per
-//     wave, lanes permuted so rows land XOR-swizzled) while the current tile is computed.  Both
-//     stay row-major ([key][head_dim], as in the pool); the P.V operand, which needs four
-//     consecutive keys of one head-dim column per lane, is read with the gfx950 transposing LDS
-//     load (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i%4 of the
-//     8-byte reads of lanes i/4, 4+i/4, 8+i/4, 12+i/4).  One barrier per tile.
+//     row tiles of one (chunk, head) read the same prefix through the same L2.
+//   * Keys go through LDS 64 at a time (four 16-token blocks) in a 4-stage ring: tile t+3 is
+//     requested while tile t is computed.  Every wave moves one 16-token block of K (waves
+//     0-3) or V (waves 4-7) per tile with four 1 KiB buffer-to-LDS loads whose descriptor
+//     covers only the block's valid rows: rows past the sequence end (and blocks past it)
+//     arrive as zeros, and every wave issues the same number of loads, so a counted wait
+//     (vmcnt) keeps the newest tile in flight across the barrier.  Lanes are permuted so rows
+//     land XOR-swizzled.  K and V stay row-major ([key][head_dim], as in the pool); the P.V
+//     operand, which needs four consecutive keys of one head-dim column per lane, is read with
+//     the gfx950 transposing LDS load (ds_read_b64_tr_b16: in each 16-lane group, lane i
+//     receives element i%4 of the 8-byte reads of lanes i/4, 4+i/4, 8+i/4, 12+i/4).
 //   * Scores are computed transposed, S^T = K Q^T, so a lane holds one query row: the running
 //     max / sum and the rescale of the output accumulator are per-lane scalars, and the
 //     probabilities are already laid out as the B operand of O^T = V^T P^T.  P is rounded to
-//     bf16 for that product; everything else stays fp32.  The running max is raised only when
-//     a row's new maximum exceeds it by more than 2^8 in probability (probabilities then stay
-//     below 256), so most tiles skip the accumulator rescale.
-//   * Masking is by selection (-inf scores; V zero-filled past the sequence end), applied only
-//     to tiles that reach past a row's position.  K past the end is left as whatever the LDS
-//     buffer held: its scores are always replaced by -inf.
+//     bf16 for that product; everything else stays fp32.  The scores of tile t+1 are issued to
+//     the matrix cores while the exponentials of tile t run on the vector ALUs.  The running
+//     max is raised only when a row's new maximum exceeds it by more than 2^8 in probability
+//     (probabilities then stay below 256), so most tiles skip the accumulator rescale.
+//   * Masking is by selection (-inf scores), applied only to tiles that reach past a row's
+//     position.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -41,13 +43,15 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kTileRows = kWaves * kRowsPerWave;   // 128
+constexpr int kTileRows = kWaves * kRowsPerWave;   // 256
 constexpr int kKvTile = 64;                         // keys per LDS tile (4 blocks)
-constexpr int kChunks = kD / 8;                     // 16-byte chunks per K row
+constexpr int kChunks = kD / 8;                     // 16-byte chunks per key row
+constexpr int kRowBytes = kD * 2;                   // 256
 constexpr int kRankCap = 128;                       // chunks ranked longest-first in-kernel
 constexpr float kLazyLog2 = 8.f;                    // rescale only past 2^8 growth
+constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -58,6 +62,7 @@ __device__ __forceinline__ int v_swz(int key, int chunk) { return chunk ^ ((key 
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Transposing LDS read of 8 bytes (gfx950 ds_read_b64_tr_b16).
 __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
@@ -67,20 +72,26 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt immediates (gfx9 layout: vmcnt low bits [3:0], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVm4 = 0x0F74;
+
 }  // namespace
 
 template <int G>
-__global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 1) void pa_prefill_kernel(
     bf16_t* __restrict__ out, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_start_loc,
     int num_chunks, int num_kv_heads, int max_blocks_per_seq, int tiles_max, float scale_log2) {
   constexpr int kTokPerTile = kTileRows / G;
-  // two buffers per operand, as distinct arrays: the loop is unrolled by two so every access
-  // names its buffer at compile time, which lets the compiler see that the direct-to-LDS loads
-  // into one buffer cannot alias the reads of the other (no wait for the prefetch)
-  __shared__ uint4 sK0[kKvTile * kChunks], sK1[kKvTile * kChunks];        // 2 x 16 KiB
-  __shared__ uint4 sV0[kKvTile * kChunks], sV1[kKvTile * kChunks];        // 2 x 16 KiB
+  // A 4-stage ring of K and V tiles, as distinct arrays (128 KiB).  The loop is unrolled by
+  // four so every access names its stage at compile time, which lets the compiler see that
+  // the loads into one stage cannot alias the reads of another.
+  __shared__ uint4 sK0[kKvTile * kChunks], sK1[kKvTile * kChunks], sK2[kKvTile * kChunks],
+      sK3[kKvTile * kChunks];
+  __shared__ uint4 sV0[kKvTile * kChunks], sV1[kKvTile * kChunks], sV2[kKvTile * kChunks],
+      sV3[kKvTile * kChunks];
   __shared__ int s_len[kRankCap];
   __shared__ int s_scan[kRankCap];
   __shared__ int s_item[2];
@@ -127,9 +138,9 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
       }
     }
     __syncthreads();
-    c = s_item[0];
+    c = wave_uniform(s_item[0]);     // uniform, so table lookups become scalar loads
     if (c < 0) return;                                   // past the last item
-    const int local = s_item[1];
+    const int local = wave_uniform(s_item[1]);
     const int n = query_start_loc[c + 1] - query_start_loc[c];
     const int tiles = (n * G + kTileRows - 1) / kTileRows;
     tile = tiles - 1 - local / num_kv_heads;
@@ -179,40 +190,30 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
   }
 
   // ------------------------------------------------------------------ tile staging
-  // Block ids of tile kt's four blocks (wave-uniform scalar loads; 0 past the table's end,
-  // never dereferenced since every load below is guarded by the sequence length).
-  auto tile_phys = [&](int kt, int (&ph)[4]) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int lb = kt * 4 + b;
-      ph[b] = lb < nblk ? wave_uniform(table[lb]) : 0;
-    }
-  };
-  auto pick = [](const int (&ph)[4], int b) {
-    return b == 0 ? ph[0] : b == 1 ? ph[1] : b == 2 ? ph[2] : ph[3];
-  };
-  // K and V: wave w fills block w of the tile (keys 16w .. 16w+15) with four 1 KiB
-  // direct-to-LDS loads each; in load j lane l writes LDS chunk (16w + 4j + l/16, l%16) and so
-  // fetches the logical chunk whose swizzled position that is.  V slots past the sequence end
-  // are zero-filled instead (p = 0 there, and 0 * garbage could be NaN); K slots there are left
-  // alone, since their scores are masked.
-  auto load_kv = [&](int kt, const int (&ph)[4], uint4* kdst, uint4* vdst) {
-    const size_t base = (static_cast<size_t>(pick(ph, wave)) * num_kv_heads + kvh) * slab;
+  // Wave w moves block (w % 4) of a tile, K for w < 4 and V otherwise.  Its descriptor covers
+  // exactly the block's valid rows, so rows past the sequence end (and blocks past it, whose
+  // table entry is not read) come in as zeros.  In load j lane l writes LDS chunk
+  // (16*blk + 4j + l/16, l%16) and so fetches the logical chunk whose swizzled position that is.
+  const int stage_blk = wave % 4;
+  const bool stage_v = wave >= 4;
+  const bf16_t* stage_pool = stage_v ? v_cache : k_cache;
+  auto load_tile = [&](int kt, uint4* kdst, uint4* vdst) {
+    const int lb = wave_uniform(kt * 4 + stage_blk);   // keeps the table read a scalar load
+    const int first = lb * kBlock;
+    const int rows = max(0, min(kBlock, L - first));
+    const int phys = lb < nblk ? wave_uniform(table[lb]) : 0;
+    const bf16_t* src = stage_pool + (static_cast<size_t>(phys) * num_kv_heads + kvh) * slab;
+    __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(src), 0, rows * kRowBytes, kRsrcWord3);
+    uint4* dst = (stage_v ? vdst : kdst) + stage_blk * kBlock * kChunks;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int slot = 4 * j + lane / 16;
-      const int key = wave * kBlock + slot;
+      const int key = stage_blk * kBlock + slot;
       const int pchunk = lane % 16;
-      uint4* kd = kdst + (wave * kBlock + 4 * j) * kChunks;
-      uint4* vd = vdst + (wave * kBlock + 4 * j) * kChunks;
-      if (kt * kKvTile + key < L) {
-        __builtin_amdgcn_global_load_lds(k_cache + base + slot * kD + k_swz(key, pchunk) * 8, kd,
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(v_cache + base + slot * kD + v_swz(key, pchunk) * 8, vd,
-                                         16, 0, 0);
-      } else {
-        vd[lane] = make_uint4(0, 0, 0, 0);
-      }
+      const int lchunk = stage_v ? v_swz(key, pchunk) : k_swz(key, pchunk);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + 4 * j * kChunks), 16,
+                                               slot * kRowBytes + lchunk * 16, 0, 0, 0);
     }
   };
 
@@ -225,42 +226,43 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
   float l_run = 0.f;
   const float lazy_raw = kLazyLog2 / scale_log2;
 
-  // one tile: prefetch tile kt+1 into the other buffers, compute tile kt, publish kt+1
-  auto step = [&](int kt, const uint4* kcur, const uint4* vcur, uint4* knext, uint4* vnext) {
-    if (kt + 1 < num_kv_tiles) {
-      int ph[4];
-      tile_phys(kt + 1, ph);
-      load_kv(kt + 1, ph, knext, vnext);
-    }
-
-    if (kt * kKvTile < kv_end_w) {
-      // --------------------------------------------------------------- S^T = K Q^T
-      // operands are read a half of the head dim at a time, then the two key subtiles'
-      // MFMAs alternate so back-to-back MFMAs never depend on each other
-      f32x16_t sacc[2];
+  // S^T = K Q^T for one 64-key tile.  Operands are read half the head dim at a time, and the
+  // two key subtiles' MFMAs alternate so back-to-back MFMAs never depend on each other.
+  auto qk = [&](const uint4* kbuf, f32x16_t (&sacc)[2]) {
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[t2][v] = 0.f;
+      for (int v = 0; v < 16; ++v) sacc[t2][v] = 0.f;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        uint4 a[2][4];
+    for (int kh = 0; kh < 2; ++kh) {
+      uint4 a[2][4];
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int key = t2 * 32 + col;
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4)
-            a[t2][k4] = kcur[key * kChunks + k_swz(key, (kh * 4 + k4) * 2 + half)];
-        }
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int key = t2 * 32 + col;
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2)
-            sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(a[t2][k4]), as_bf16x8(qreg[kh * 4 + k4]), sacc[t2], 0, 0, 0);
+          a[t2][k4] = kbuf[key * kChunks + k_swz(key, (kh * 4 + k4) * 2 + half)];
       }
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+          sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(a[t2][k4]), as_bf16x8(qreg[kh * 4 + k4]), sacc[t2], 0, 0, 0);
+    }
+  };
 
-      // --------------------------------------------------------------- online softmax
+  // One step of the pipeline, for tile kt whose scores are already in `cur`:
+  //   request tile kt+3 into the free stage; issue the QK MFMAs of tile kt+1 into `nxt` while
+  //   the softmax of tile kt runs on the vector ALUs; O^T += V(kt)^T P(kt)^T; then wait until
+  //   only tile kt+3 is still in flight (tile kt+2 is what the next step reads) and publish.
+  // Tile t lives in stage t % 4.  A request past the last tile loads only zeros.
+  auto step = [&](int kt, const uint4* knext, const uint4* vcur, uint4* kload, uint4* vload,
+                  f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    load_tile(kt + 3, kload, vload);
+
+    if (kt * kKvTile < kv_end_w) {
+      // --------------------------------------------------------------- online softmax (max)
       const bool need_mask = kt * kKvTile + kKvTile - 1 > prefix + t_lo_w;
       if (need_mask) {
 #pragma unroll
@@ -268,14 +270,14 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = kt * kKvTile + t2 * 32 + (v / 4) * 8 + half * 4 + (v % 4);
-            sacc[t2][v] = key <= pos ? sacc[t2][v] : kNegInf;
+            cur[t2][v] = key <= pos ? cur[t2][v] : kNegInf;
           }
       }
-      float mx = sacc[0][0];
+      float mx = cur[0][0];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[t2][v]);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, cur[t2][v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // raise the running max only when some row of the wave grew past the lazy margin
       if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy_raw) != 0) {
@@ -288,14 +290,21 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
       }
+
+      // scores of the next tile (independent of what follows, so the matrix cores run while
+      // the exponentials below are computed); a wave that needs no key of tile kt needs none of
+      // tile kt+1 either, and past the last tile the result is simply never used
+      qk(knext, nxt);
+
+      // --------------------------------------------------------------- probabilities
       const float mc = m_run * scale_log2;
       float psum = 0.f;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(fmaf(sacc[t2][v], scale_log2, -mc));
-          sacc[t2][v] = p;
+          const float p = fast_exp2(fmaf(cur[t2][v], scale_log2, -mc));
+          cur[t2][v] = p;
           psum += p;
         }
       l_run += psum;
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
       uint4 pT[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f32x16_t& p = sacc[s / 2];
+        const f32x16_t& p = cur[s / 2];
         const int o = (s % 2) * 8;
         pT[s] = make_uint4(pack_bf16x2(p[o + 0], p[o + 1]), pack_bf16x2(p[o + 2], p[o + 3]),
                            pack_bf16x2(p[o + 4], p[o + 5]), pack_bf16x2(p[o + 6], p[o + 7]));
@@ -339,22 +348,32 @@ __global__ __launch_bounds__(kThreads, 2) void pa_prefill_kernel(
       }
     }
 
-    __builtin_amdgcn_s_waitcnt(0);    // the direct-to-LDS loads have landed
-    __syncthreads();
+    // every wave issued exactly four loads per step: the newest four (tile kt+3) may stay
+    // in flight, everything older (tile kt+2, read next step) must have landed.  A bare
+    // s_barrier, not __syncthreads: its memory fence would wait for the prefetch as well.
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_barrier();
   };
 
-  // prologue: tile 0 into buffers 0
-  {
-    int ph[4];
-    tile_phys(0, ph);
-    load_kv(0, ph, sK0, sV0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // prologue: tiles 0, 1, 2 requested; tiles 0 and 1 landed; scores of tile 0
+  load_tile(0, sK0, sV0);
+  load_tile(1, sK1, sV1);
+  load_tile(2, sK2, sV2);
+  __builtin_amdgcn_s_waitcnt(kWaitVm4);
+  __builtin_amdgcn_s_barrier();
+  f32x16_t sa[2], sb[2];
+  qk(sK0, sa);
+  for (int kt = 0; kt < num_kv_tiles; kt += 4) {
+    step(kt, sK1, sV0, sK3, sV3, sa, sb);
+    if (kt + 1 >= num_kv_tiles) break;
+    step(kt + 1, sK2, sV1, sK0, sV0, sb, sa);
+    if (kt + 2 >= num_kv_tiles) break;
+    step(kt + 2, sK3, sV2, sK1, sV1, sa, sb);
+    if (kt + 3 >= num_kv_tiles) break;
+    step(kt + 3, sK0, sV3, sK2, sV2, sb, sa);
   }
-  for (int kt = 0; kt < num_kv_tiles; kt += 2) {
-    step(kt, sK0, sV0, sK1, sV1);
-    if (kt + 1 < num_kv_tiles) step(kt + 1, sK1, sV1, sK0, sV0);
-  }
+  // no load may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // ------------------------------------------------------------------------- write out
   const float l_tot = l_run + __shfl_xor(l_run, 32);
