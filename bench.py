@@ -119,7 +119,7 @@ def decode_callable(b):
     out = torch.empty_like(b.q)
     ws_n = ops.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
                                         16, msl)
-    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_n, 16), dtype=torch.uint8, device="cuda")
 
     def fn():
         ops.pa_decode(out, b.q, b.k_cache, b.v_cache, bt, sl, msl, b.scale, workspace=ws)
@@ -173,7 +173,25 @@ def bench_mixed(steps, warmup):
         prefill()
         dfn()
 
+    # The same step with the chunks and the decodes, which are independent once the append
+    # has landed, on two streams (both at the default priority), joined before the step ends.
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def step_overlapped():
+        append()
+        appended = torch.cuda.Event()
+        appended.record(main)
+        side.wait_event(appended)
+        with torch.cuda.stream(side):
+            prefill()
+        dfn()
+        chunks_done = torch.cuda.Event()
+        chunks_done.record(side)
+        main.wait_event(chunks_done)
+
     t_step = time_calls(step, steps, warmup)
+    t_over = time_calls(step_overlapped, steps, warmup)
     t_app = time_calls(append, steps, warmup)
     t_pre = time_calls(prefill, steps, warmup)
     t_dec = time_calls(dfn, steps, warmup)
@@ -184,11 +202,14 @@ def bench_mixed(steps, warmup):
     tflops = flops / (t_pre[0] * 1e-3) / 1e12
     res = dict(
         tokens_per_s=T / (t_step[0] * 1e-3), ms_per_step=t_step[0], new_tokens=T,
+        overlapped_tokens_per_s=T / (t_over[0] * 1e-3), overlapped_ms_per_step=t_over[0],
         append_ms=t_app[0], append_gbps=app_bytes / (t_app[0] * 1e-3) / 1e9,
         prefill_ms=t_pre[0], prefill_gflop=flops / 1e9, prefill_tflops=tflops,
         prefill_mfma_frac=tflops / BF16_PEAK_TFLOPS,
         decode_ms=t_dec[0], decode_kv_bytes=dec_bytes,
         decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9)
+    log(f"mixed step, chunks and decodes on two streams: {t_over[0] * 1e3:.1f} us -> "
+        f"{res['overlapped_tokens_per_s']:.0f} tok/s")
     log(f"mixed step: {t_step[0] * 1e3:.1f} us -> {res['tokens_per_s']:.0f} tok/s | append "
         f"{t_app[0] * 1e3:.1f} us | prefill {t_pre[0] * 1e3:.1f} us {tflops:.0f} TFLOP/s "
         f"({100 * res['prefill_mfma_frac']:.1f}% MFMA) | decode {t_dec[0] * 1e3:.1f} us "
