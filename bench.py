@@ -119,7 +119,7 @@ def decode_callable(b):
     out = torch.empty_like(b.q)
     ws_n = ops.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
                                         16, msl)
-    ws = torch.zeros(max(ws_n, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda")
 
     def fn():
         ops.pa_decode(out, b.q, b.k_cache, b.v_cache, bt, sl, msl, b.scale, workspace=ws)
@@ -144,7 +144,7 @@ def chunk_flops(prefixes, chunk_lens, num_q_heads, head_dim) -> float:
     return 4.0 * head_dim * num_q_heads * tot
 
 
-def bench_mixed(steps, warmup):
+def bench_mixed(steps, warmup, overlap=False):
     m = W.mixed_bf16(device="cuda", poison=False)
     nb = m.k_cache.shape[0]
     checks.check_slots(m.slot_mapping, nb, 16)
@@ -191,7 +191,7 @@ def bench_mixed(steps, warmup):
         main.wait_event(chunks_done)
 
     t_step = time_calls(step, steps, warmup)
-    t_over = time_calls(step_overlapped, steps, warmup)
+    t_over = time_calls(step_overlapped, steps, warmup) if overlap else None
     t_app = time_calls(append, steps, warmup)
     t_pre = time_calls(prefill, steps, warmup)
     t_dec = time_calls(dfn, steps, warmup)
@@ -202,14 +202,16 @@ def bench_mixed(steps, warmup):
     tflops = flops / (t_pre[0] * 1e-3) / 1e12
     res = dict(
         tokens_per_s=T / (t_step[0] * 1e-3), ms_per_step=t_step[0], new_tokens=T,
-        overlapped_tokens_per_s=T / (t_over[0] * 1e-3), overlapped_ms_per_step=t_over[0],
+
         append_ms=t_app[0], append_gbps=app_bytes / (t_app[0] * 1e-3) / 1e9,
         prefill_ms=t_pre[0], prefill_gflop=flops / 1e9, prefill_tflops=tflops,
         prefill_mfma_frac=tflops / BF16_PEAK_TFLOPS,
         decode_ms=t_dec[0], decode_kv_bytes=dec_bytes,
         decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9)
-    log(f"mixed step, chunks and decodes on two streams: {t_over[0] * 1e3:.1f} us -> "
-        f"{res['overlapped_tokens_per_s']:.0f} tok/s")
+    if t_over is not None:
+        res.update(overlapped_tokens_per_s=T / (t_over[0] * 1e-3), overlapped_ms_per_step=t_over[0])
+        log(f"mixed step, chunks and decodes on two streams: {t_over[0] * 1e3:.1f} us -> "
+            f"{res['overlapped_tokens_per_s']:.0f} tok/s")
     log(f"mixed step: {t_step[0] * 1e3:.1f} us -> {res['tokens_per_s']:.0f} tok/s | append "
         f"{t_app[0] * 1e3:.1f} us | prefill {t_pre[0] * 1e3:.1f} us {tflops:.0f} TFLOP/s "
         f"({100 * res['prefill_mfma_frac']:.1f}% MFMA) | decode {t_dec[0] * 1e3:.1f} us "
@@ -292,6 +294,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams")
+    ap.add_argument("--overlap-mixed", action="store_true",
+                    help="also time the mixed step with chunks and decodes on two streams")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain MIB-MiB device copy (for scaling rocprofv3 counters)")
     args = ap.parse_args()
@@ -320,7 +324,7 @@ def main():
 
     extra = {}
     if "mixed" not in skip:
-        extra["mixed_batch"] = bench_mixed(max(steps // 2, 5), warmup)
+        extra["mixed_batch"] = bench_mixed(max(steps // 2, 5), warmup, args.overlap_mixed)
         torch.cuda.empty_cache()
     if "long" not in skip:
         lb = W.long_bf16(device="cuda", poison=False)

@@ -29,7 +29,7 @@
  * Ownership: the caller owns every buffer.  Device pointers must be device memory of the
  * current HIP device; `stream` is a hipStream_t (NULL = the default stream).  The library never
  * allocates or frees memory, keeps no pointer after returning, and holds no mutable global state,
- * so calls from several host threads are safe (each with its own decode workspace).  Every call only enqueues work on `stream`: no
+ * so calls from several host threads are safe.  Every call only enqueues work on `stream`: no
  * host synchronisation, no device-to-host copy.
  *
  * Errors: host scalars and pointers are checked before anything is enqueued; a failed check
@@ -72,10 +72,7 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  *   max_seq_len  host upper bound of seq_lens; sizes the split grid (no device read-back)
  *   scale        multiplies q.k before the softmax; finite and > 0
  *   workspace    device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL
- *                when that size is 0).  It must be zero-filled before its first use; every
- *                call leaves it zero-filled again where it matters (per-sequence counters of
- *                finished splits), so one zeroing at allocation suffices.  It belongs to one
- *                call at a time: calls that share a workspace must not overlap.
+ *                when that size is 0); contents need no initialisation
  *
  * Supported: head_dim in {64, 128, 256}; block_size 16; num_q_heads/num_kv_heads in
  * {1, 2, 4, 8}; dtype F32 or BF16.  Pointers 16-byte aligned.
@@ -87,8 +84,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                     pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pa_decode needs for these sizes (0 when no sequence can need a second
- * split, which is when max_seq_len fits one split). */
+/* Bytes of workspace pa_decode needs for these sizes (0 when no split is needed). */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len);
 

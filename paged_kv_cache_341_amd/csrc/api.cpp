@@ -68,24 +68,11 @@ int plan_blocks_per_split(int num_seqs, int num_kv_heads, int group, int max_seq
   return std::min(bps, std::max(nblk, 1));
 }
 
-// Decode workspace: [counters: S*Hkv uint32][ml: S*Hq*nsplit*2 fp32][acc: S*Hq*nsplit*D fp32],
-// each region 256-byte aligned.  Empty when no sequence can need more than one split.
-struct DecodeWsLayout {
-  size_t cnt_off, ml_off, acc_off, total;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-DecodeWsLayout decode_ws_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                int nsplit) {
-  DecodeWsLayout l{0, 0, 0, 0};
-  if (nsplit <= 1) return l;
+size_t decode_ws_bytes(int num_seqs, int num_q_heads, int head_dim, int nsplit) {
+  if (nsplit <= 1) return 0;
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * nsplit;
-  l.cnt_off = 0;
-  l.ml_off = align256(static_cast<size_t>(num_seqs) * num_kv_heads * sizeof(uint32_t));
-  l.acc_off = l.ml_off + align256(rows * 2 * sizeof(float));
-  l.total = l.acc_off + rows * head_dim * sizeof(float);
-  return l;
+  const size_t ml = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+  return ml + rows * head_dim * sizeof(float);
 }
 
 pa_status device_status(hipError_t e, const char* what) {
@@ -119,7 +106,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, max_seq_len);
   const int nblk = (max_seq_len + block_size - 1) / block_size;
   const int nsplit = (nblk + bps - 1) / bps;
-  return decode_ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, nsplit).total;
+  return decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -155,9 +142,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, max_seq_len);
   const int nblk = (max_seq_len + block_size - 1) / block_size;
   const int nsplit = (nblk + bps - 1) / bps;
-  const DecodeWsLayout ws = decode_ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             nsplit);
-  const size_t need = ws.total;
+  const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_decode: workspace %zu bytes, need %zu",
                 workspace_bytes, need);
@@ -174,10 +159,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  char* wsb = static_cast<char*>(workspace);
-  a.ws_cnt = need ? reinterpret_cast<uint32_t*>(wsb + ws.cnt_off) : nullptr;
-  a.ws_ml = need ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
-  a.ws_acc = need ? reinterpret_cast<float*>(wsb + ws.acc_off) : nullptr;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * nsplit;
+  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             ((rows * 2 * sizeof(float) + 255) & ~size_t(255)))
+                  : nullptr;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;

@@ -17,7 +17,6 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* ws_ml;        // [S][Hq][nsplit_max][2]  (max in log2 units, sum)
   float* ws_acc;       // [S][Hq][nsplit_max][D]
-  uint32_t* ws_cnt;    // [S][Hkv] splits finished; zero between calls
   int num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq;
   int bps, nsplit_max;
   float scale_log2;

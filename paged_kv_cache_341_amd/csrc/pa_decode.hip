@@ -15,9 +15,8 @@
 //   phase 3  each wave reads the V slabs of the same blocks and accumulates p * V in fp32,
 //            lanes split over the head dimension again; waves are summed through LDS.
 // A split with the whole sequence writes the normalised output; otherwise it writes
-// (max, sum, unnormalised acc) to the workspace, and the last split of the (sequence, kv head)
-// to finish (a counter in the workspace) combines all splits in split order (log-sum-exp
-// weighting), so results do not depend on scheduling and one launch does the whole call.
+// (max, sum, unnormalised acc) and a merge kernel combines the splits in split order
+// (log-sum-exp weighting), so results do not depend on scheduling.
 // Only the last block of a sequence can be partly filled; its unfilled slots are masked by
 // selection (score -inf, V treated as 0), never by multiplying, so garbage there is harmless.
 #include "device_common.hpp"
@@ -78,76 +77,12 @@ __device__ __forceinline__ void store_out(bf16_t* p, float v) {
   p->bits = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
 }
 
-// Relaxed agent-scope accesses (the sc1 bit on gfx950): coherent across the XCDs' L2 caches by
-// themselves, so split partials need no cache write-back or invalidation to be exchanged.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Combine the splits of one (sequence, query head) row with one wave.  Lanes first read the
-// per-split (max, sum) pairs in parallel, so the split count costs one round trip rather than
-// a chain of dependent loads; then each lane owns D/64 output elements and sums the splits'
-// weighted partial numerators in split order (the same order on every run).
-template <typename T, int D>
-__device__ __forceinline__ void merge_row(T* __restrict__ out, const float* __restrict__ ws_ml,
-                                          const float* __restrict__ ws_acc, size_t row,
-                                          int nsplit, int nsplit_max, int lane) {
-  constexpr int kPer = D / kWave;
-  const float* ml = ws_ml + row * nsplit_max * 2;
-  const float* acc = ws_acc + row * nsplit_max * D;
-  float M = kNegInf;
-  for (int i = lane; i < nsplit; i += kWave) M = fmaxf(M, load_coherent(ml + 2 * i));
-  M = group_max<kWave>(M);
-  float den = 0.f;
-  for (int i = lane; i < nsplit; i += kWave)
-    den = fmaf(exp2f(load_coherent(ml + 2 * i) - M), load_coherent(ml + 2 * i + 1), den);
-  den = group_sum<kWave>(den);
-  const float inv = 1.f / den;
-
-  float num[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
-  for (int c = 0; c < nsplit; c += kWave) {
-    const int i = c + lane;
-    const float w = i < nsplit ? exp2f(load_coherent(ml + 2 * i) - M) : 0.f;   // split weight
-    const int cnt = min(kWave, nsplit - c);
-    int k = 0;
-    for (; k + 4 <= cnt; k += 4) {
-      float a[4][kPer];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-          a[u][e] = load_coherent(acc + static_cast<size_t>(c + k + u) * D + lane + e * kWave);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wu = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), k + u));
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) num[e] = fmaf(wu, a[u][e], num[e]);
-      }
-    }
-    for (; k < cnt; ++k) {
-      const float wk = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), k));
-#pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        num[e] = fmaf(wk, load_coherent(acc + static_cast<size_t>(c + k) * D + lane + e * kWave),
-                      num[e]);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) store_out(out + row * D + lane + e * kWave, num[e] * inv);
-}
-
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-    uint32_t* __restrict__ ws_cnt, const T* __restrict__ q, const T* __restrict__ k_cache,
-    const T* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ seq_lens, int num_kv_heads, int max_blocks_per_seq, int bps,
-    int nsplit_max, float scale_log2) {
+    const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    int num_kv_heads, int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2) {
   using S = DecodeShape<T, D, G>;
   constexpr int kEpc = S::kEpc;
   constexpr int kCpr = S::kCpr;
@@ -157,7 +92,6 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   __shared__ float red[kDecodeWaves][G];
   __shared__ float stat_m[G];
   __shared__ float stat_l[G];
-  __shared__ int is_last;
 
   // grid.x runs over (sequence, kv head) and grid.y over splits, so consecutive workgroups
   // belong to different kv heads.  Workgroups are dealt to the 8 XCDs round-robin in launch
@@ -348,35 +282,76 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     if (nsplit_seq == 1) {
       store_out(out + row * D + d, a / stat_l[h]);
     } else {
-      store_coherent(ws_acc + (row * nsplit_max + split) * D + d, a);
+      ws_acc[(row * nsplit_max + split) * D + d] = a;
       if (d == 0) {
-        store_coherent(ws_ml + (row * nsplit_max + split) * 2 + 0, stat_m[h]);
-        store_coherent(ws_ml + (row * nsplit_max + split) * 2 + 1, stat_l[h]);
+        ws_ml[(row * nsplit_max + split) * 2 + 0] = stat_m[h];
+        ws_ml[(row * nsplit_max + split) * 2 + 1] = stat_l[h];
       }
     }
   }
-  if (nsplit_seq == 1) return;
+}
 
-  // The last split of this (sequence, kv head) to finish merges all of them.  The partials
-  // went out as agent-scope coherent stores; each thread waits until its stores have completed
-  // before the workgroup bumps the counter (also agent-scope), and the merging workgroup reads
-  // them back with agent-scope loads.  It then resets the counter, so the workspace is left as
-  // it was found (all counters zero).
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  uint32_t* counter = ws_cnt + static_cast<size_t>(s) * num_kv_heads + kvh;
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              static_cast<uint32_t>(nsplit_seq - 1);
-  __syncthreads();
-  if (!is_last) return;
-  for (int h = wave; h < G; h += kDecodeWaves)
-    merge_row<T, D>(out, ws_ml, ws_acc, static_cast<size_t>(s) * Hq + kvh * G + h, nsplit_seq,
-                    nsplit_max, lane);
-  if (threadIdx.x == 0)
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Combine the splits of one (sequence, query head) row; one wave per row.  Lanes first read
+// the per-split (max, sum) pairs in parallel, so the split count costs one round trip rather
+// than a chain of dependent loads; then each lane owns D/64 output elements and sums the
+// splits' weighted partial numerators in split order (the same order on every run).
+constexpr int kMergeWaves = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
+    T* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+    const int32_t* __restrict__ seq_lens, int num_rows, int num_q_heads, int bps,
+    int nsplit_max) {
+  constexpr int kPer = D / kWave;
+  const int row = blockIdx.x * kMergeWaves + static_cast<int>(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  if (row >= num_rows) return;
+  const int s = row / num_q_heads;
+  const int L = seq_lens[s];
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int nsplit = (nblk + bps - 1) / bps;
+  if (nsplit <= 1) return;
+  const float* ml = ws_ml + static_cast<size_t>(row) * nsplit_max * 2;
+  const float* acc = ws_acc + static_cast<size_t>(row) * nsplit_max * D;
+
+  float M = kNegInf;
+  for (int i = lane; i < nsplit; i += kWave) M = fmaxf(M, ml[2 * i]);
+  M = group_max<kWave>(M);
+  float den = 0.f;
+  for (int i = lane; i < nsplit; i += kWave) den = fmaf(exp2f(ml[2 * i] - M), ml[2 * i + 1], den);
+  den = group_sum<kWave>(den);
+  const float inv = 1.f / den;
+
+  float num[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  for (int c = 0; c < nsplit; c += kWave) {
+    const int i = c + lane;
+    const float w = i < nsplit ? exp2f(ml[2 * i] - M) : 0.f;   // this lane's split weight
+    const int cnt = min(kWave, nsplit - c);
+    int k = 0;
+    for (; k + 4 <= cnt; k += 4) {
+      float a[4][kPer];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a[u][e] = acc[static_cast<size_t>(c + k + u) * D + lane + e * kWave];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), k + u));
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) num[e] = fmaf(wu, a[u][e], num[e]);
+      }
+    }
+    for (; k < cnt; ++k) {
+      const float wk = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), k));
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        num[e] = fmaf(wk, acc[static_cast<size_t>(c + k) * D + lane + e * kWave], num[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) store_out(out + static_cast<size_t>(row) * D + lane + e * kWave, num[e] * inv);
 }
 
 template <typename T, int D, int G>
@@ -385,10 +360,17 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
   const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * kBlock * G,
                                       static_cast<size_t>(kDecodeWaves) * G * D) * sizeof(float);
   hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G>), grid, dim3(kDecodeThreads), lds,
-                     a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.ws_cnt,
+                     a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_tables, a.seq_lens,
                      a.num_kv_heads, a.max_blocks_per_seq, a.bps, a.nsplit_max, a.scale_log2);
+  if (a.nsplit_max > 1) {
+    const int rows = a.num_seqs * a.num_kv_heads * G;
+    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D>),
+                       dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
+                       a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens, rows,
+                       a.num_kv_heads * G, a.bps, a.nsplit_max);
+  }
   return hipGetLastError();
 }
 

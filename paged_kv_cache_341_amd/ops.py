@@ -119,10 +119,7 @@ def pa_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
 def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """out[s, h] = attention of q[s, h] over sequence s's cached tokens (see pagedattn.h).
-
-    A caller-provided `workspace` must have been zero-filled before its first use (e.g.
-    torch.zeros); each call leaves it reusable."""
+    """out[s, h] = attention of q[s, h] over sequence s's cached tokens (see pagedattn.h)."""
     lib = load_library()
     _contig(out, q, k_cache, v_cache, block_tables, seq_lens)
     _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
@@ -134,8 +131,7 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
     _need(out.dtype == q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
     ws_need = pa_decode_workspace_size(S, Hq, Hkv, D, B, max_seq_len)
     if workspace is None and ws_need:
-        # zero-filled once; pa_decode leaves its split counters at zero after every call
-        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                        _ptr(seq_lens), S, Hq, Hkv, D, B, NB, block_tables.shape[1],
