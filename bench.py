@@ -114,11 +114,11 @@ def kv_bytes(seq_lens, num_kv_heads, head_dim, elem_bytes=2) -> int:
 
 def decode_callable(b):
     msl = int(b.seq_lens.max())
-    checks.check_tables(b.block_tables, b.seq_lens, b.k_cache.shape[0], 16, msl)
+    checks.check_tables(b.block_tables, b.seq_lens, b.k_cache.shape[0], b.block_size, msl)
     bt, sl = i32(b.block_tables), i32(b.seq_lens)
     out = torch.empty_like(b.q)
     ws_n = ops.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
-                                        16, msl)
+                                        b.block_size, msl)
     ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda")
 
     def fn():
@@ -257,6 +257,33 @@ def bench_beams(steps, warmup):
     return res
 
 
+def sweep_block_size(steps, warmup):
+    """Decode bandwidth against block size, with physical blocks scattered (a seeded random free
+    list) or laid out contiguously per sequence, on the 64-sequence batch and the long context;
+    plus the tail waste (slots allocated but holding no token) each block size costs."""
+    res = {}
+    for name, make in (("decode_bf16", W.decode_bf16), ("long_bf16", W.long_bf16)):
+        for B in (8, 16, 32, 64):
+            row = {}
+            for scatter in (True, False):
+                b = make(device="cuda", poison=False, block_size=B, scatter=scatter)
+                r = bench_decode(b, steps, warmup, f"{name} B={B} "
+                                 f"{'scattered' if scatter else 'contiguous'}")
+                row["scattered_gbps" if scatter else "contiguous_gbps"] = round(r["gbps"], 1)
+                row["scattered_us" if scatter else "contiguous_us"] = round(r["ms"] * 1e3, 2)
+                lens = b.seq_lens.astype(np.int64)
+                row["tail_waste_frac"] = round(float(((-(-lens // B)) * B - lens).sum()
+                                                     / lens.sum()), 5)
+                del b
+                torch.cuda.empty_cache()
+            row["paged_over_contiguous_time"] = round(row["scattered_us"] / row["contiguous_us"], 4)
+            res[f"{name}/B{B}"] = row
+            log(f"  {name} B={B}: scattered {row['scattered_gbps']} GB/s, contiguous "
+                f"{row['contiguous_gbps']} GB/s, paged/contiguous time "
+                f"{row['paged_over_contiguous_time']}, tail waste {row['tail_waste_frac']}")
+    return res
+
+
 def cpu_baseline(seconds: float = 10.0):
     """The fp64 oracle on the host cores, over whole passes of the decode batch (same generator,
     CPU copy of the inputs) until about `seconds` have been spent."""
@@ -294,6 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams")
+    ap.add_argument("--sweep-block-size", action="store_true",
+                    help="also sweep block sizes 8/16/32/64, scattered vs contiguous blocks")
     ap.add_argument("--overlap-mixed", action="store_true",
                     help="also time the mixed step with chunks and decodes on two streams")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -335,6 +364,8 @@ def main():
     if "beams" not in skip:
         extra["beam_step"] = bench_beams(max(steps // 2, 5), warmup)
         torch.cuda.empty_cache()
+    if args.sweep_block_size:
+        extra["block_size_sweep"] = sweep_block_size(max(steps // 2, 5), warmup)
 
     result = {
         "metric": METRIC,

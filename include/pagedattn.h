@@ -74,7 +74,8 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  *   workspace    device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL
  *                when that size is 0); contents need no initialisation
  *
- * Supported: head_dim in {64, 128, 256}; block_size 16; num_q_heads/num_kv_heads in
+ * Supported: head_dim in {64, 128, 256}; block_size in {8, 16, 32, 64} (16 is the pages'
+ * default; the others serve the block-size trade-off); num_q_heads/num_kv_heads in
  * {1, 2, 4, 8}; dtype F32 or BF16.  Pointers 16-byte aligned.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -43,25 +43,31 @@ bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 constexpr int kSupportedBlock = 16;
 
-// Blocks per decode split.  Aims for roughly kTargetGroups workgroups when every sequence is as
-// long as max_seq_len, with 16..64 blocks each; the LDS score buffer caps it at 512/G blocks.
-// PA_DECODE_SPLIT_BLOCKS overrides it (tuning aid).
-int plan_blocks_per_split(int num_seqs, int num_kv_heads, int group, int max_seq_len) {
-  const int nblk = (max_seq_len + kSupportedBlock - 1) / kSupportedBlock;
+// Block sizes the decode kernels are built for (tokens per block).
+bool decode_block_supported(int b) { return b == 8 || b == 16 || b == 32 || b == 64; }
+
+// Blocks per decode split.  A split covers 256, 512 or 1024 tokens, the smallest that keeps
+// the number of workgroups near kTargetGroups when every sequence is max_seq_len long; the LDS
+// score buffer caps a split at 8192/G tokens.  PA_DECODE_SPLIT_BLOCKS overrides the block
+// count (tuning aid).
+int plan_blocks_per_split(int num_seqs, int num_kv_heads, int group, int block_size,
+                          int max_seq_len) {
+  const int nblk = (max_seq_len + block_size - 1) / block_size;
   static const int env = [] {
     const char* e = std::getenv("PA_DECODE_SPLIT_BLOCKS");
     return e ? std::atoi(e) : 0;
   }();
-  const int cap = 512 / group;
+  const int cap = std::max(1, 8192 / group / block_size);
   int bps;
   if (env > 0) {
     bps = env;
   } else {
     constexpr long kTargetGroups = 4096;
-    const long want = (static_cast<long>(nblk) * num_seqs * num_kv_heads + kTargetGroups - 1) /
-                      kTargetGroups;
-    bps = 16;
-    while (bps < want && bps < 64) bps *= 2;
+    const long want_tokens = (static_cast<long>(max_seq_len) * num_seqs * num_kv_heads +
+                              kTargetGroups - 1) / kTargetGroups;
+    int tokens = 256;
+    while (tokens < want_tokens && tokens < 1024) tokens *= 2;
+    bps = std::max(1, tokens / block_size);
   }
   bps = std::min(bps, cap);
   bps = std::max(bps, 1);
@@ -100,10 +106,11 @@ const char* pa_last_error(void) { return g_last_error.c_str(); }
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size != kSupportedBlock || max_seq_len <= 0 || num_q_heads % num_kv_heads != 0)
+      !decode_block_supported(block_size) || max_seq_len <= 0 ||
+      num_q_heads % num_kv_heads != 0)
     return 0;
   const int g = num_q_heads / num_kv_heads;
-  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, max_seq_len);
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, max_seq_len);
   const int nblk = (max_seq_len + block_size - 1) / block_size;
   const int nsplit = (nblk + bps - 1) / bps;
   return decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
@@ -133,13 +140,14 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode: scale must be finite and positive");
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (supported: 64, 128, 256)", head_dim);
-  if (block_size != kSupportedBlock)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (supported: 16)", block_size);
+  if (!decode_block_supported(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (supported: 8, 16, 32, 64)",
+                block_size);
   const int g = num_q_heads / num_kv_heads;
   if (!supported_group(g))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per kv head (supported: 1,2,4,8)",
                 g);
-  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, max_seq_len);
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, max_seq_len);
   const int nblk = (max_seq_len + block_size - 1) / block_size;
   const int nsplit = (nblk + bps - 1) / bps;
   const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
@@ -168,6 +176,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
+  a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.bps = bps;
   a.nsplit_max = nsplit;

@@ -17,7 +17,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* ws_ml;        // [S][Hq][nsplit_max][2]  (max in log2 units, sum)
   float* ws_acc;       // [S][Hq][nsplit_max][D]
-  int num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int bps, nsplit_max;
   float scale_log2;
   bool bf16;

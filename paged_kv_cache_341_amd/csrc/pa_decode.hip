@@ -24,7 +24,7 @@
 
 namespace pa {
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int B>
 struct DecodeShape {
   static constexpr int kEpc = Elem<T>::kPerChunk;   // elements per 16-byte chunk
   static constexpr int kCpr = D / kEpc;             // chunks per token row
@@ -32,20 +32,21 @@ struct DecodeShape {
   static constexpr int kW1 = 8;
   static constexpr int kR1 = kCpr / kW1;
   static constexpr int kGr1 = kWave / kW1;           // token groups per wave
-  static constexpr int kTpb1 = kBlock / kGr1;        // tokens per group per block
+  static constexpr int kTpb1 = B / kGr1;             // tokens per group per block
   // phase 3 (p * V): kW3 lanes share a token row, kR3 chunks each
   static constexpr int kW3 = kCpr >= 16 ? 16 : kCpr;
   static constexpr int kR3 = kCpr / kW3;
   static constexpr int kGr3 = kWave / kW3;
-  static constexpr int kTpb3 = kBlock / kGr3;
+  static constexpr int kTpb3 = B / kGr3;
   static constexpr int kAcc = kR3 * kEpc;            // fp32 accumulators per head per lane
   static_assert(kCpr % kW1 == 0 && kCpr % kW3 == 0, "head_dim not supported");
   static_assert(kTpb1 >= 1 && kTpb3 >= 1, "bad lane split");
+  // blocks whose loads a wave keeps in flight together: 64 tokens' worth
+  static constexpr int kBatch = B >= 64 ? 1 : 64 / B;
 };
 
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = kDecodeWaves * kWave;
-constexpr int kDecodeBatch = 4;   // blocks whose loads a wave keeps in flight together
 
 // Partial dot product of one 16-byte chunk of q with one chunk of K.
 __device__ __forceinline__ float chunk_dot(uint4 q, uint4 k, float acc, bf16_t) {
@@ -77,13 +78,15 @@ __device__ __forceinline__ void store_out(bf16_t* p, float v) {
   p->bits = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int B>
 __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     int num_kv_heads, int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2) {
-  using S = DecodeShape<T, D, G>;
+  using S = DecodeShape<T, D, G, B>;
+  constexpr int kBlock = B;
+  constexpr int kDecodeBatch = S::kBatch;
   constexpr int kEpc = S::kEpc;
   constexpr int kCpr = S::kCpr;
   const T tag{};
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
 // splits' weighted partial numerators in split order (the same order on every run).
 constexpr int kMergeWaves = 4;
 
-template <typename T, int D>
+template <typename T, int D, int B>
 __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
     T* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
     const int32_t* __restrict__ seq_lens, int num_rows, int num_q_heads, int bps,
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   if (row >= num_rows) return;
   const int s = row / num_q_heads;
   const int L = seq_lens[s];
-  const int nblk = (L + kBlock - 1) / kBlock;
+  const int nblk = (L + B - 1) / B;
   const int nsplit = (nblk + bps - 1) / bps;
   if (nsplit <= 1) return;
   const float* ml = ws_ml + static_cast<size_t>(row) * nsplit_max * 2;
@@ -354,24 +357,35 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   for (int e = 0; e < kPer; ++e) store_out(out + static_cast<size_t>(row) * D + lane + e * kWave, num[e] * inv);
 }
 
-template <typename T, int D, int G>
-hipError_t launch_decode_t(const DecodeArgs& a) {
+template <typename T, int D, int G, int B>
+hipError_t launch_decode_tb(const DecodeArgs& a) {
   const dim3 grid(a.num_seqs * a.num_kv_heads, a.nsplit_max);
-  const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * kBlock * G,
+  const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * B * G,
                                       static_cast<size_t>(kDecodeWaves) * G * D) * sizeof(float);
-  hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G>), grid, dim3(kDecodeThreads), lds,
+  hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G, B>), grid, dim3(kDecodeThreads), lds,
                      a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_tables, a.seq_lens,
                      a.num_kv_heads, a.max_blocks_per_seq, a.bps, a.nsplit_max, a.scale_log2);
   if (a.nsplit_max > 1) {
     const int rows = a.num_seqs * a.num_kv_heads * G;
-    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D>),
+    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D, B>),
                        dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
                        a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens, rows,
                        a.num_kv_heads * G, a.bps, a.nsplit_max);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t launch_decode_t(const DecodeArgs& a) {
+  switch (a.block_size) {
+    case 8: return launch_decode_tb<T, D, G, 8>(a);
+    case 16: return launch_decode_tb<T, D, G, 16>(a);
+    case 32: return launch_decode_tb<T, D, G, 32>(a);
+    case 64: return launch_decode_tb<T, D, G, 64>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>

@@ -150,21 +150,29 @@ def _filled_slots(bm: BlockManager, seq_ids: Sequence[int], num_blocks: int, blo
     return filled
 
 
-def _permuted_manager(rng: np.random.Generator, num_blocks: int, block_size: int) -> BlockManager:
-    return BlockManager(num_blocks, block_size, free_order=rng.permutation(num_blocks))
+def _permuted_manager(rng: np.random.Generator, num_blocks: int, block_size: int,
+                      scatter: bool = True) -> BlockManager:
+    """Free list in a seeded random order (scattered physical ids), or in id order, which lays
+    every sequence's blocks out contiguously (the permutation is drawn either way, so the
+    values drawn afterwards do not depend on the choice)."""
+    order = rng.permutation(num_blocks)
+    return BlockManager(num_blocks, block_size,
+                        free_order=order if scatter else np.arange(num_blocks))
 
 
 def make_decode(seq_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
                 dtype: str, seed: int, *, block_size: int = BLOCK_SIZE,
                 num_blocks: Optional[int] = None, pool_factor: float = 1.2,
                 rng: Optional[np.random.Generator] = None, poison: bool = True,
-                device="cpu", scale: Optional[float] = None, name: str = "") -> DecodeBatch:
-    """A decode batch over the given lengths, blocks handed out from a permuted free list."""
+                device="cpu", scale: Optional[float] = None, name: str = "",
+                scatter: bool = True) -> DecodeBatch:
+    """A decode batch over the given lengths, blocks handed out from a permuted free list
+    (``scatter=False``: in id order, so each sequence's blocks are physically contiguous)."""
     rng = np.random.default_rng(seed) if rng is None else rng
     lens = [int(x) for x in seq_lens]
     need = sum(blocks_for(n, block_size) for n in lens)
     nb = int(num_blocks) if num_blocks is not None else max(1, math.ceil(pool_factor * need))
-    bm = _permuted_manager(rng, nb, block_size)
+    bm = _permuted_manager(rng, nb, block_size, scatter)
     for i, n in enumerate(lens):
         bm.add_sequence(i, n)
     tables = bm.block_tables(range(len(lens)))
@@ -191,20 +199,23 @@ def tiny_f32(device="cpu", poison: bool = True, seed: int = SEED_BASE + 1) -> De
 
 
 def decode_bf16(device="cpu", poison: bool = True, seed: int = SEED_BASE + 2,
-                num_seqs: int = 64, lo: int = 128, hi: int = 4096) -> DecodeBatch:
+                num_seqs: int = 64, lo: int = 128, hi: int = 4096,
+                block_size: int = BLOCK_SIZE, scatter: bool = True) -> DecodeBatch:
     """Workload 2: 64 sequences, lengths U[128, 4096], 32/8 heads, head_dim 128, bf16."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi + 1, size=num_seqs)
     return make_decode(lens, 32, 8, 128, "bf16", seed, rng=rng, poison=poison, device=device,
-                       name="decode_bf16")
+                       name="decode_bf16", block_size=block_size, scatter=scatter)
 
 
 def long_bf16(device="cpu", poison: bool = True, seed: int = SEED_BASE + 3,
-              num_seqs: int = 32, seq_len: int = 32768) -> DecodeBatch:
+              num_seqs: int = 32, seq_len: int = 32768, block_size: int = BLOCK_SIZE,
+              scatter: bool = True) -> DecodeBatch:
     """Workload 3: 32 sequences x 32768 tokens, 16/4 heads, head_dim 256, bf16."""
     rng = np.random.default_rng(seed)
     return make_decode([seq_len] * num_seqs, 16, 4, 256, "bf16", seed, rng=rng, poison=poison,
-                       device=device, name="long_bf16")
+                       device=device, name="long_bf16", block_size=block_size,
+                       scatter=scatter)
 
 
 def mixed_bf16(device="cpu", poison: bool = True, seed: int = SEED_BASE + 4,

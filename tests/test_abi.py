@@ -54,7 +54,7 @@ def _decode(**kw):
     (dict(q=None), INV), (dict(S=0), INV), (dict(Hq=6, Hkv=4), INV), (dict(maxlen=129), INV),
     (dict(out=P + 2), INV), (dict(dtype=7), INV), (dict(scale=float("nan")), INV),
     (dict(scale=0.0), INV), (dict(scale=-0.1), INV), (dict(scale=float("inf")), INV),
-    (dict(D=96), UNS), (dict(B=8, MB=16), UNS), (dict(Hq=32, Hkv=2), UNS),
+    (dict(D=96), UNS), (dict(B=4, MB=32), UNS), (dict(B=128, MB=1), UNS), (dict(Hq=32, Hkv=2), UNS),
     (dict(maxlen=128 * 16, MB=128, S=64, wsb=16), WS),
 ])
 def test_decode_rejects(kw, status):

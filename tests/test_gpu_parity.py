@@ -67,6 +67,22 @@ def test_decode_f32_ragged(G, D):
     assert_close(widen(out), oracle_decode(b), F32_ATOL, F32_RTOL, f"f32 G{G} D{D}")
 
 
+@pytest.mark.parametrize("B", [8, 32, 64])
+def test_decode_other_block_sizes(B):
+    """Block sizes 8, 32 and 64 (16 is the default everywhere else): ragged lengths around
+    block edges, NaN in every unfilled slot, G = 4, and an fp32 case."""
+    lens = [1, B - 1, B, B + 1, 3 * B + 5, 700, 2047, 4100]
+    say(f"case: bf16 decode, block size {B}")
+    b = W.make_decode(lens, 16, 4, 128, "bf16", seed=1600 + B, device=DEV, block_size=B)
+    out = run_decode(b)
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, f"block size {B}")
+    tab = int(b.block_tables[0, 0])
+    for h in range(16):
+        assert torch.equal(out[0, h], b.v_cache[tab, h // 4, 0])
+    f = W.make_decode(lens[:6], 4, 2, 64, "f32", seed=1700 + B, device=DEV, block_size=B)
+    assert_close(widen(run_decode(f)), oracle_decode(f), F32_ATOL, F32_RTOL, f"f32 B{B}")
+
+
 def test_decode_bf16_full_batch():
     say("case: decode_bf16 full size (64 seqs, U[128,4096], 32/8, D128)")
     b = W.decode_bf16(device=DEV)
