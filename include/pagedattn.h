@@ -90,6 +90,43 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len);
 
 /*
+ * pa_decode_grouped - pa_decode for a batch whose sequences come in groups that share a
+ * prefix of physical blocks: parallel samples or beams forked from one prompt hold the same
+ * blocks until a write forces a copy (study-docs "PagedAttention & Continuous Batching",
+ * section "Copy-on-write"; cloudmash "Batching and PagedAttention", section "Sharing blocks").
+ * The result equals pa_decode's on the same arguments (up to fp32 summation order); the shared
+ * blocks are read once per group instead of once per member, and the group's query rows attend
+ * to them together on MFMA.
+ *
+ *   group_start   [num_groups+1] int32, rising from 0 to num_seqs: group g is the sequences
+ *                 group_start[g] .. group_start[g+1]-1 (a group of one is allowed)
+ *   shared_blocks [num_seqs] int32: the number of leading blocks the sequence shares with its
+ *                 group; equal within a group, and table entries 0 .. shared_blocks-1 equal
+ *                 within a group (only the group's first table is read for them).  Clamped
+ *                 on the device to 0 .. floor(seq_lens/block_size): only full blocks are shared.
+ *   max_group_size host upper bound of group sizes
+ *   other arguments as pa_decode; workspace of pa_decode_grouped_workspace_size(...) bytes,
+ *   contents need no initialisation
+ *
+ * Supported: dtype BF16, head_dim 128, block_size 16, num_q_heads/num_kv_heads in
+ * {1, 2, 4, 8}.  Arguments that break the equalities above give wrong values, never an
+ * access outside the buffers the other arguments describe.
+ */
+pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* group_start, const int32_t* shared_blocks,
+                            int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_seq_len, float scale, pa_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode_grouped needs for these sizes (0 for unsupported sizes). */
+size_t pa_decode_grouped_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_seq_len);
+
+/*
  * pa_prefill_chunk - attention for chunks of new prompt tokens over a paged prefix
  * (cloudmash "Continuous batching": long prompts are processed in chunks across steps).
  * Chunk c owns packed query rows query_start_loc[c] .. query_start_loc[c+1]-1; its sequence

@@ -227,6 +227,40 @@ class BlockManager:
             self._release(blk)
 
 
+def shared_prefix_groups(block_tables: np.ndarray, seq_lens: np.ndarray, block_size: int,
+                         max_group: int = 64) -> Tuple[np.ndarray, np.ndarray, int]:
+    """Group a decode batch by shared leading blocks, for the grouped decode.
+
+    Consecutive sequences whose first table entries are the same physical block (forks of one
+    parent: parallel samples, beams) form a group; its shared prefix is the number of leading
+    entries equal across all members, limited to each member's full blocks (a partly filled
+    block is never shared by the time its holders decode: the first write copied it).  Groups
+    are cut at ``max_group`` members.  Sequences with no shared full block stay in groups of
+    one with a prefix of 0.  Returns (group_start [G+1], shared_blocks [S], largest group).
+    """
+    tables = np.asarray(block_tables)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    S = lens.shape[0]
+    full = lens // block_size
+    starts = [0]
+    shared = np.zeros(S, dtype=np.int32)
+    i = 0
+    while i < S:
+        j = i + 1
+        while (j < S and j - i < max_group and full[i] > 0 and full[j] > 0
+               and tables[j, 0] == tables[i, 0]):
+            j += 1
+        if j - i > 1:
+            n = int(min(full[i:j]))
+            same = np.all(tables[i:j, :n] == tables[i, :n], axis=0)
+            n = int(np.argmin(same)) if not same.all() else n
+            shared[i:j] = n
+        starts.append(j)
+        i = j
+    gs = np.asarray(starts, dtype=np.int32)
+    return gs, shared, int(np.max(np.diff(gs))) if S else 0
+
+
 def kv_bytes_per_token(num_kv_heads: int, head_dim: int, elem_bytes: int, num_layers: int = 1) -> int:
     """K plus V bytes one token occupies across ``num_layers`` layers."""
     return 2 * num_kv_heads * head_dim * elem_bytes * num_layers

@@ -25,6 +25,31 @@ def check_tables(block_tables: np.ndarray, seq_lens: np.ndarray, num_blocks: int
             raise ValueError(f"sequence {s}: block id out of range")
 
 
+def check_groups(group_start: np.ndarray, shared_blocks: np.ndarray, block_tables: np.ndarray,
+                 seq_lens: np.ndarray, block_size: int, max_group_size: int) -> None:
+    """The grouped decode's preconditions: groups cover the batch in order, and each group's
+    members agree on the shared prefix and its block ids, which are full blocks of every
+    member.  (The kernels clamp what they read, so a breach gives wrong values, not faults.)"""
+    gs = np.asarray(group_start, dtype=np.int64)
+    sb = np.asarray(shared_blocks, dtype=np.int64)
+    bt = np.asarray(block_tables)
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    S = sl.shape[0]
+    if gs.ndim != 1 or gs.size < 2 or gs[0] != 0 or gs[-1] != S or np.any(np.diff(gs) < 1):
+        raise ValueError("group_start must rise strictly from 0 to num_seqs")
+    if np.diff(gs).max() > max_group_size:
+        raise ValueError("a group is larger than max_group_size")
+    if sb.shape != (S,) or sb.min() < 0 or np.any(sb * block_size > sl):
+        raise ValueError("shared_blocks must lie in [0, seq_len // block_size]")
+    for g in range(gs.size - 1):
+        a, b = int(gs[g]), int(gs[g + 1])
+        n = int(sb[a])
+        if np.any(sb[a:b] != n):
+            raise ValueError(f"group {g}: members disagree on shared_blocks")
+        if n and np.any(bt[a:b, :n] != bt[a, :n]):
+            raise ValueError(f"group {g}: members' shared table entries differ")
+
+
 def check_chunks(query_start_loc: np.ndarray, seq_lens: np.ndarray, total_q: int,
                  max_q_len: int) -> None:
     qsl = np.asarray(query_start_loc, dtype=np.int64)

@@ -180,10 +180,163 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.bps = bps;
   a.nsplit_max = nsplit;
+  a.nsplit_tail = nsplit;
+  a.skip_blocks = nullptr;
+  a.slot_base = 0;
+  a.shared_split_keys = 1;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.bf16 = dtype == PA_DTYPE_BF16;
   a.stream = static_cast<hipStream_t>(stream);
   return device_status(pa::launch_decode(a), "pa_decode launch");
+}
+
+// ------------------------------------------------------------------------- grouped decode
+namespace {
+
+constexpr int kSharedSplitKeys = 512;   // shared keys per shared-prefix work item
+// the shared-prefix kernel keeps a split's block ids one per lane and loads 32 keys per tile
+static_assert(kSharedSplitKeys % 32 == 0 && kSharedSplitKeys <= 64 * 16, "shared split size");
+
+struct GroupedPlan {
+  int bps, nsplit_shared, nsplit_tail, nsplit_max;
+  size_t ml_bytes, total;
+};
+
+GroupedPlan plan_grouped(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_seq_len) {
+  GroupedPlan p{};
+  const int g = num_q_heads / num_kv_heads;
+  p.bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, max_seq_len);
+  const int nblk = (max_seq_len + block_size - 1) / block_size;
+  p.nsplit_tail = (nblk + p.bps - 1) / p.bps;
+  p.nsplit_shared = (max_seq_len + kSharedSplitKeys - 1) / kSharedSplitKeys;
+  p.nsplit_max = p.nsplit_shared + p.nsplit_tail;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.nsplit_max;
+  p.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+  p.total = p.ml_bytes + rows * head_dim * sizeof(float);
+  return p;
+}
+
+}  // namespace
+
+size_t pa_decode_grouped_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_seq_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size != kSupportedBlock || max_seq_len <= 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  return plan_grouped(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len)
+      .total;
+}
+
+pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* group_start, const int32_t* shared_blocks,
+                            int32_t num_seqs, int32_t num_groups, int32_t max_group_size,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_seq_len, float scale, pa_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !group_start ||
+      !shared_blocks)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: null pointer argument");
+  if (num_seqs <= 0 || num_groups <= 0 || max_group_size <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_seq_len <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: sizes must be positive");
+  if (num_groups > num_seqs || max_group_size > num_seqs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: more groups or members than "
+                "sequences");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: num_q_heads %d not a multiple of "
+                "num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (!valid_dtype(dtype))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: unknown dtype");
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: max_seq_len exceeds table capacity");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: buffers must be 16-byte aligned");
+  if (!(scale > 0.f) || scale == __builtin_inff())
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: scale must be finite and positive");
+  if (dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: only bf16 is supported");
+  if (head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: head_dim %d (supported: 128)",
+                head_dim);
+  if (block_size != kSupportedBlock)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: block_size %d (supported: 16)",
+                block_size);
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_group(g))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: %d query heads per kv head "
+                "(supported: 1,2,4,8)", g);
+  const GroupedPlan p =
+      plan_grouped(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_decode_grouped: workspace %zu bytes, need %zu",
+                workspace_bytes, p.total);
+  if (!aligned16(workspace))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: workspace must be 16-byte aligned");
+  const int row_tiles = (max_group_size * g + 31) / 32;
+  if (p.nsplit_max > 65535 || static_cast<int64_t>(num_seqs) * num_kv_heads > (int64_t{1} << 24) ||
+      static_cast<int64_t>(num_groups) * row_tiles * num_kv_heads > (int64_t{1} << 26))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: grid too large");
+
+  float* ws_ml = static_cast<float*>(workspace);
+  float* ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ml_bytes);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  pa::SharedPrefixArgs sp{};
+  sp.ws_ml = ws_ml;
+  sp.ws_acc = ws_acc;
+  sp.q = q;
+  sp.k_cache = k_cache;
+  sp.v_cache = v_cache;
+  sp.block_tables = block_tables;
+  sp.group_start = group_start;
+  sp.shared_blocks = shared_blocks;
+  sp.seq_lens = seq_lens;
+  sp.num_seqs = num_seqs;
+  sp.num_groups = num_groups;
+  sp.num_q_heads = num_q_heads;
+  sp.num_kv_heads = num_kv_heads;
+  sp.max_blocks_per_seq = max_blocks_per_seq;
+  sp.row_tiles = row_tiles;
+  sp.nsplit_shared = p.nsplit_shared;
+  sp.split_keys = kSharedSplitKeys;
+  sp.slot_base = p.nsplit_shared;
+  sp.nsplit_max = p.nsplit_max;
+  sp.scale_log2 = scale_log2;
+  sp.stream = st;
+  hipError_t e = pa::launch_shared_prefix(sp);
+  if (e != hipSuccess) return device_status(e, "pa_decode_grouped shared-prefix launch");
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.ws_ml = ws_ml;
+  a.ws_acc = ws_acc;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.bps = p.bps;
+  a.nsplit_max = p.nsplit_max;
+  a.nsplit_tail = p.nsplit_tail;
+  a.skip_blocks = shared_blocks;
+  a.slot_base = p.nsplit_shared;
+  a.shared_split_keys = kSharedSplitKeys;
+  a.scale_log2 = scale_log2;
+  a.bf16 = true;
+  a.stream = st;
+  return device_status(pa::launch_decode(a), "pa_decode_grouped launch");
 }
 
 size_t pa_prefill_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }

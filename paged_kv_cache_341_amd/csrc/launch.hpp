@@ -17,6 +17,12 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* ws_ml;        // [S][Hq][nsplit_max][2]  (max in log2 units, sum)
   float* ws_acc;       // [S][Hq][nsplit_max][D]
+  // Grouped decode (a prefix shared inside each group of sequences, done by the shared-prefix
+  // kernel): per-sequence leading blocks to skip (null for plain decode), the slot where the
+  // split kernel's partials start, and the keys per shared-prefix split.
+  const int32_t* skip_blocks;
+  int slot_base, shared_split_keys;
+  int nsplit_tail;     // grid.y of the split kernel
   int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int bps, nsplit_max;
   float scale_log2;
@@ -57,6 +63,24 @@ struct CowArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
+
+struct SharedPrefixArgs {
+  float* ws_ml;
+  float* ws_acc;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* group_start;    // [num_groups + 1]
+  const int32_t* shared_blocks;  // [num_seqs]
+  const int32_t* seq_lens;       // [num_seqs]
+  int num_seqs, num_groups, num_q_heads, num_kv_heads, max_blocks_per_seq;
+  int row_tiles, nsplit_shared, split_keys, slot_base, nsplit_max;
+  float scale_log2;
+  hipStream_t stream;
+};
+
+hipError_t launch_shared_prefix(const SharedPrefixArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_append(const AppendArgs& a);
 hipError_t launch_cow(const CowArgs& a);

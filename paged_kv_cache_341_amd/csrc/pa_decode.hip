@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
-    int num_kv_heads, int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2) {
+    const int32_t* __restrict__ skip_blocks, int slot_base, int num_kv_heads,
+    int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2) {
   using S = DecodeShape<T, D, G, B>;
   constexpr int kBlock = B;
   constexpr int kDecodeBatch = S::kBatch;
@@ -106,11 +107,14 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   const int split = blockIdx.y;
   const int L = seq_lens[s];
   const int nblk = (L + kBlock - 1) / kBlock;
-  const int b_begin = split * bps;
+  // leading blocks another kernel covers (a prefix shared with the sequence's group)
+  const int skip = skip_blocks ? min(max(skip_blocks[s], 0), L / kBlock) : 0;
+  const int b_begin = skip + split * bps;
   if (b_begin >= nblk) return;
   const int b_end = min(nblk, b_begin + bps);
   const int ntok = min(L, b_end * kBlock) - b_begin * kBlock;
-  const int nsplit_seq = (nblk + bps - 1) / bps;
+  const int nsplit_seq = (nblk - skip + bps - 1) / bps;
+  const bool direct = skip == 0 && nsplit_seq == 1;   // the whole sequence in this split
   const int wave = wave_uniform(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int Hq = num_kv_heads * G;
@@ -282,13 +286,14 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w) a += wacc[(w * G + h) * D + d];
     const size_t row = static_cast<size_t>(s) * Hq + kvh * G + h;
-    if (nsplit_seq == 1) {
+    if (direct) {
       store_out(out + row * D + d, a / stat_l[h]);
     } else {
-      ws_acc[(row * nsplit_max + split) * D + d] = a;
+      const size_t slot = row * nsplit_max + slot_base + split;
+      ws_acc[slot * D + d] = a;
       if (d == 0) {
-        ws_ml[(row * nsplit_max + split) * 2 + 0] = stat_m[h];
-        ws_ml[(row * nsplit_max + split) * 2 + 1] = stat_l[h];
+        ws_ml[slot * 2 + 0] = stat_m[h];
+        ws_ml[slot * 2 + 1] = stat_l[h];
       }
     }
   }
@@ -303,7 +308,8 @@ constexpr int kMergeWaves = 4;
 template <typename T, int D, int B>
 __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
     T* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-    const int32_t* __restrict__ seq_lens, int num_rows, int num_q_heads, int bps,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ skip_blocks,
+    int slot_base, int shared_split_keys, int num_rows, int num_q_heads, int bps,
     int nsplit_max) {
   constexpr int kPer = D / kWave;
   const int row = blockIdx.x * kMergeWaves + static_cast<int>(threadIdx.x / kWave);
@@ -312,10 +318,15 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   const int s = row / num_q_heads;
   const int L = seq_lens[s];
   const int nblk = (L + B - 1) / B;
-  const int nsplit = (nblk + bps - 1) / bps;
-  if (nsplit <= 1) return;
-  const float* ml = ws_ml + static_cast<size_t>(row) * nsplit_max * 2;
-  const float* acc = ws_acc + static_cast<size_t>(row) * nsplit_max * D;
+  // partials of this row: the shared-prefix splits end at slot_base, the splits of the rest
+  // start there, so they form one range
+  const int skip = skip_blocks ? min(max(skip_blocks[s], 0), L / B) : 0;
+  const int ns = skip > 0 ? (skip * B + shared_split_keys - 1) / shared_split_keys : 0;
+  const int nt = (nblk - skip + bps - 1) / bps;
+  if (ns == 0 && nt <= 1) return;                 // written directly by the split kernel
+  const int nsplit = ns + nt;
+  const float* ml = ws_ml + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * 2;
+  const float* acc = ws_acc + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * D;
 
   float M = kNegInf;
   for (int i = lane; i < nsplit; i += kWave) M = fmaxf(M, ml[2 * i]);
@@ -359,19 +370,21 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
 
 template <typename T, int D, int G, int B>
 hipError_t launch_decode_tb(const DecodeArgs& a) {
-  const dim3 grid(a.num_seqs * a.num_kv_heads, a.nsplit_max);
   const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * B * G,
                                       static_cast<size_t>(kDecodeWaves) * G * D) * sizeof(float);
-  hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G, B>), grid, dim3(kDecodeThreads), lds,
-                     a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc,
+  const dim3 grid_split(a.num_seqs * a.num_kv_heads, a.nsplit_tail);
+  hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G, B>), grid_split, dim3(kDecodeThreads),
+                     lds, a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_tables, a.seq_lens,
-                     a.num_kv_heads, a.max_blocks_per_seq, a.bps, a.nsplit_max, a.scale_log2);
+                     a.skip_blocks, a.slot_base, a.num_kv_heads, a.max_blocks_per_seq, a.bps,
+                     a.nsplit_max, a.scale_log2);
   if (a.nsplit_max > 1) {
     const int rows = a.num_seqs * a.num_kv_heads * G;
     hipLaunchKernelGGL((pa_decode_merge_kernel<T, D, B>),
                        dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
-                       a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens, rows,
+                       a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens,
+                       a.skip_blocks, a.slot_base, a.shared_split_keys, rows,
                        a.num_kv_heads * G, a.bps, a.nsplit_max);
   }
   return hipGetLastError();

@@ -34,47 +34,23 @@
 //     (probabilities then stay below 256), so most tiles skip the accumulator rescale.
 //   * Masking is by selection (-inf scores), applied only to tiles that reach past a row's
 //     position.
-#include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma_tiles.hpp"
 
 namespace pa {
 
 namespace {
 
-constexpr int kD = 128;
+constexpr int kD = kTileD;
 constexpr int kRowsPerWave = 32;
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kTileRows = kWaves * kRowsPerWave;   // 256
 constexpr int kKvTile = 64;                         // keys per LDS tile (4 blocks)
-constexpr int kChunks = kD / 8;                     // 16-byte chunks per key row
-constexpr int kRowBytes = kD * 2;                   // 256
+constexpr int kChunks = kTileChunks;
+constexpr int kRowBytes = kTileRowBytes;
 constexpr int kRankCap = 128;                       // chunks ranked longest-first in-kernel
 constexpr float kLazyLog2 = 8.f;                    // rescale only past 2^8 growth
-constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Swizzles of the row-major LDS tiles, in 16-byte chunks of a 256-byte key row.  K rows are
-// read one chunk per lane down 32 keys, V rows eight keys at a time by the transposing load.
-__device__ __forceinline__ int k_swz(int key, int chunk) { return chunk ^ (key & 15); }
-__device__ __forceinline__ int v_swz(int key, int chunk) { return chunk ^ ((key & 3) << 2); }
-
-typedef __attribute__((ext_vector_type(4))) short i16x4_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Transposing LDS read of 8 bytes (gfx950 ds_read_b64_tr_b16).
-__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// s_waitcnt immediates (gfx9 layout: vmcnt low bits [3:0], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm4 = 0x0F74;
 
 }  // namespace
 

@@ -23,7 +23,8 @@ PA_DTYPE_BF16 = 1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED",
                 3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_DEVICE"}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_prefill_chunk",
+EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_grouped",
+            "pa_decode_grouped_workspace_size", "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
             "pa_last_error", "pa_hbm_read_probe")
 
@@ -53,6 +54,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               _i32, _i32, _f32, ctypes.c_int, _vp, _sz, _vp]
     lib.pa_decode_workspace_size.restype = _sz
     lib.pa_decode_workspace_size.argtypes = [_i32] * 6
+    lib.pa_decode_grouped.restype = ctypes.c_int
+    lib.pa_decode_grouped.argtypes = [_vp] * 8 + [_i32] * 10 + [_f32, ctypes.c_int, _vp, _sz,
+                                                                _vp]
+    lib.pa_decode_grouped_workspace_size.restype = _sz
+    lib.pa_decode_grouped_workspace_size.argtypes = [_i32] * 6
     lib.pa_prefill_chunk.restype = ctypes.c_int
     lib.pa_prefill_chunk.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp] + [_i32] * 10 + \
         [_f32, ctypes.c_int, _vp, _sz, _vp]
@@ -137,6 +143,43 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        _ptr(seq_lens), S, Hq, Hkv, D, B, NB, block_tables.shape[1],
                        int(max_seq_len), float(scale), _dtype_code(q), _ptr(workspace),
                        ws_bytes, _stream(q, stream))
+    _check(st)
+    return out
+
+
+def pa_decode_grouped_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, block_size: int, max_seq_len: int) -> int:
+    return int(load_library().pa_decode_grouped_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len))
+
+
+def pa_decode_grouped(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                      group_start: torch.Tensor, shared_blocks: torch.Tensor,
+                      max_group_size: int, max_seq_len: int, scale: float,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """pa_decode for sequences grouped by a shared block prefix (see pagedattn.h)."""
+    lib = load_library()
+    _contig(out, q, k_cache, v_cache, block_tables, seq_lens, group_start, shared_blocks)
+    _need(all(t.dtype == torch.int32 for t in (block_tables, seq_lens, group_start,
+                                                shared_blocks)),
+          "block_tables, seq_lens, group_start and shared_blocks must be int32")
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    _need(D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape), "cache shape mismatch")
+    _need(tuple(out.shape) == tuple(q.shape), "out must match q")
+    _need(out.dtype == q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+    _need(shared_blocks.numel() == S, "shared_blocks needs one entry per sequence")
+    ws_need = pa_decode_grouped_workspace_size(S, Hq, Hkv, D, B, max_seq_len)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_grouped(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_tables), _ptr(seq_lens), _ptr(group_start),
+                               _ptr(shared_blocks), S, group_start.numel() - 1,
+                               int(max_group_size), Hq, Hkv, D, B, NB, block_tables.shape[1],
+                               int(max_seq_len), float(scale), _dtype_code(q), _ptr(workspace),
+                               ws_bytes, _stream(q, stream))
     _check(st)
     return out
 

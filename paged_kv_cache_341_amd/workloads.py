@@ -39,7 +39,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from .block_manager import BlockManager, blocks_for
+from .block_manager import BlockManager, blocks_for, shared_prefix_groups
 
 SEED_BASE = 3410
 BLOCK_SIZE = 16
@@ -72,6 +72,7 @@ class DecodeBatch:
     block_size: int
     dtype: str
     name: str = ""
+    extra: dict = field(default_factory=dict)
 
     @property
     def num_seqs(self) -> int:
@@ -189,6 +190,53 @@ def make_decode(seq_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, he
                        scale=default_scale(head_dim) if scale is None else f32(scale),
                        num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                        block_size=block_size, dtype=dtype, name=name)
+
+
+def make_grouped_decode(groups: Sequence[tuple], num_q_heads: int, num_kv_heads: int,
+                        head_dim: int, seed: int, *, dtype: str = "bf16", poison: bool = True,
+                        device="cpu") -> DecodeBatch:
+    """A decode batch of forked groups: ``groups`` lists (prefix_len, [tail_len per member]).
+    Each group's parent holds ``prefix_len`` tokens, is forked to the other members, and then
+    every member appends its tail (members 1.. first, the parent last, as in a beam step), so
+    a partly filled last prefix block is copied for all members but the parent.  Block ids come
+    from a permuted free list.  ``extra`` holds the group plan of ``shared_prefix_groups``."""
+    rng = np.random.default_rng(seed)
+    need = 0
+    for prefix, tails in groups:
+        need += blocks_for(prefix, BLOCK_SIZE)
+        need += sum(blocks_for(prefix + t, BLOCK_SIZE) - prefix // BLOCK_SIZE for t in tails)
+    nb = max(1, math.ceil(1.2 * need) + 1)
+    bm = _permuted_manager(rng, nb, BLOCK_SIZE)
+    seq_ids = []
+    sid = 0
+    for prefix, tails in groups:
+        root = sid
+        bm.add_sequence(root, prefix)
+        members = [root + m for m in range(len(tails))]
+        for m in members[1:]:
+            bm.fork(root, m)
+        for m, t in list(zip(members, tails))[1:] + [(root, tails[0])]:
+            if t:
+                bm.append_tokens(m, int(t))
+        seq_ids += members
+        sid += len(tails)
+    tables = bm.block_tables(seq_ids)
+    lens = np.asarray([bm.seq_len(s) for s in seq_ids], dtype=np.int32)
+    gen = _gen(seed, device)
+    q = _randn((len(seq_ids), num_q_heads, head_dim), gen, dtype, device)
+    k = _randn((nb, num_kv_heads, BLOCK_SIZE, head_dim), gen, dtype, device)
+    v = _randn((nb, num_kv_heads, BLOCK_SIZE, head_dim), gen, dtype, device)
+    if poison:
+        filled = _filled_slots(bm, seq_ids, nb, BLOCK_SIZE)
+        _poison_pool(k, filled)
+        _poison_pool(v, filled)
+    group_start, shared_blocks, max_group = shared_prefix_groups(tables, lens, BLOCK_SIZE)
+    return DecodeBatch(q=q, k_cache=k, v_cache=v, block_tables=tables, seq_lens=lens,
+                       scale=default_scale(head_dim), num_q_heads=num_q_heads,
+                       num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=BLOCK_SIZE,
+                       dtype=dtype, name="grouped",
+                       extra={"group_start": group_start, "shared_blocks": shared_blocks,
+                              "max_group_size": max_group})
 
 
 def tiny_f32(device="cpu", poison: bool = True, seed: int = SEED_BASE + 1) -> DecodeBatch:

@@ -68,6 +68,22 @@ def run_decode(batch, max_seq_len=None, device="cuda", out=None):
     return out
 
 
+def run_decode_grouped(batch, group_start, shared_blocks, max_group_size, max_seq_len=None,
+                       device="cuda", out=None, workspace=None):
+    """pa_decode_grouped on a workloads.DecodeBatch with a group plan."""
+    msl = int(batch.seq_lens.max()) if max_seq_len is None else int(max_seq_len)
+    checks.check_tables(batch.block_tables, batch.seq_lens, batch.k_cache.shape[0],
+                        batch.block_size, msl)
+    checks.check_groups(group_start, shared_blocks, batch.block_tables, batch.seq_lens,
+                        batch.block_size, max_group_size)
+    out = torch.empty_like(batch.q) if out is None else out
+    ops.pa_decode_grouped(out, batch.q, batch.k_cache, batch.v_cache,
+                          dev_i32(batch.block_tables, device), dev_i32(batch.seq_lens, device),
+                          dev_i32(group_start, device), dev_i32(shared_blocks, device),
+                          int(max_group_size), msl, batch.scale, workspace=workspace)
+    return out
+
+
 def run_prefill(q, k_cache, v_cache, tables, seq_lens, qsl, scale, device="cuda"):
     total_q = q.shape[0]
     max_q = int(np.diff(qsl).max())

@@ -70,6 +70,37 @@ def test_decode_workspace_sizes():
     assert ops.pa_decode_workspace_size(4, 6, 4, 64, 16, 100) == 0   # invalid ratio
 
 
+def _grouped(**kw):
+    a = dict(out=P, q=P, k=P, v=P, bt=P, sl=P, gs=P, sb=P, S=16, NG=2, MG=8, Hq=32, Hkv=8,
+             D=128, B=16, NB=1000, MB=300, maxlen=4300, scale=0.1, dtype=1, ws=P, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    lib = ops.load_library()
+    return lib.pa_decode_grouped(a["out"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["gs"],
+                                 a["sb"], a["S"], a["NG"], a["MG"], a["Hq"], a["Hkv"], a["D"],
+                                 a["B"], a["NB"], a["MB"], a["maxlen"], a["scale"], a["dtype"],
+                                 a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gs=None), INV), (dict(sb=None), INV), (dict(NG=0), INV), (dict(NG=17), INV),
+    (dict(MG=17), INV), (dict(MG=0), INV), (dict(Hq=30), INV), (dict(maxlen=300 * 16 + 1), INV),
+    (dict(scale=0.0), INV), (dict(ws=P + 4), INV), (dict(dtype=0), UNS), (dict(D=64), UNS),
+    (dict(B=32, MB=150), UNS), (dict(Hq=128), UNS), (dict(wsb=64), WS), (dict(ws=None), WS),
+])
+def test_grouped_decode_rejects(kw, status):
+    assert _grouped(**kw) == status
+    assert ops.load_library().pa_last_error().decode().startswith("pa_decode_grouped")
+
+
+def test_grouped_workspace_size():
+    n = ops.pa_decode_grouped_workspace_size(128, 32, 8, 128, 16, 4400)
+    # every row holds its shared-prefix splits and its own splits
+    assert n >= 128 * 32 * (4400 // 512 + 1) * (128 + 2) * 4
+    assert ops.pa_decode_grouped_workspace_size(128, 32, 8, 128, 32, 4400) == 0
+    assert ops.pa_decode_grouped_workspace_size(4, 6, 4, 128, 16, 100) == 0
+
+
 def _prefill(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, sl=P, qsl=P, C=8, T=4096, maxq=512, maxlen=8704,
              Hq=32, Hkv=8, D=128, B=16, NB=1000, MB=600, scale=0.1, dtype=1)

@@ -11,8 +11,10 @@ import torch
 from oracle import paged_ref as ref
 from paged_kv_cache_341_amd import workloads as W
 from paged_kv_cache_341_amd import ops
+from paged_kv_cache_341_amd.block_manager import shared_prefix_groups
 from tests.gpu_util import (ATOL, F32_ATOL, F32_RTOL, RTOL, assert_close, compact, dev_i32, raw,
-                            run_append, run_cow, run_decode, run_prefill, say, widen)
+                            run_append, run_cow, run_decode, run_decode_grouped, run_prefill, say,
+                            widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -166,6 +168,53 @@ def test_decode_workspace_reused_across_calls():
         assert_close(widen(out), oracle_decode(x), ATOL, RTOL, "reused workspace")
 
 
+# ------------------------------------------------------------------------------ grouped decode
+# (prefix, [tail per member]) per group: 8 forks over three shared splits (512, 512, 176 keys)
+# with a copied partial block; a single sequence; 3 identical forks whose every block is
+# shared (no own blocks left); 4 forks that share no full block; 2 forks sharing one block;
+# 5 forks over 2057 tokens (5 x G rows: two row tiles at G = 8).
+GROUPS = [(1200, [5, 1, 16, 33, 100, 0, 2, 700]), (300, [20]), (640, [0, 0, 0]),
+          (5, [30, 1, 2, 3]), (17, [1, 15]), (2057, [3, 64, 129, 1, 250])]
+
+
+def grouped(b, **kw):
+    return run_decode_grouped(b, b.extra["group_start"], b.extra["shared_blocks"],
+                              b.extra["max_group_size"], **kw)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_grouped_matches_oracle(G):
+    say(f"case: grouped decode, 6 groups, G={G}")
+    b = W.make_grouped_decode(GROUPS, 2 * G, 2, 128, seed=1700 + G, device=DEV)
+    assert b.extra["shared_blocks"].tolist()[:8] == [75] * 8
+    out = grouped(b)
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, f"grouped G{G}")
+
+
+def test_decode_grouped_deterministic_with_dirty_workspace():
+    """Two calls, the second with a workspace full of garbage, give the same bits; a larger
+    declared max_seq_len (more split slots per row) gives the same bits too."""
+    say("case: grouped decode, dirty workspace and declared max len")
+    b = W.make_grouped_decode(GROUPS, 8, 2, 128, seed=1750, device=DEV)
+    out1 = grouped(b)
+    n = ops.pa_decode_grouped_workspace_size(b.num_seqs, 8, 2, 128, 16, b.max_seq_len)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV)
+    out2 = grouped(b, workspace=ws)
+    assert torch.equal(out1, out2)
+    b.block_tables = np.pad(b.block_tables, ((0, 0), (0, 200)), constant_values=-1)
+    out3 = grouped(b, max_seq_len=b.max_seq_len + 3000)
+    assert_close(widen(out3), widen(out1), 1e-6, 1e-6, "declared max len")
+
+
+def test_decode_grouped_no_sharing_equals_plain():
+    """With every group of one (nothing shared), the grouped call is the plain decode."""
+    say("case: grouped decode with singleton groups only")
+    b = W.make_decode([1, 17, 300, 513, 2049], 8, 2, 128, "bf16", seed=1760, device=DEV)
+    S = b.num_seqs
+    out = run_decode_grouped(b, np.arange(S + 1, dtype=np.int32), np.zeros(S, np.int32), 1)
+    assert torch.equal(out, run_decode(b))
+
+
 # ------------------------------------------------------------------------------ prefill
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_prefill_ragged_chunks(G):
@@ -313,3 +362,9 @@ def test_beam_step_full_size():
     want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
                           "bf16")
     assert_close(widen(out), want, ATOL, RTOL, "beams decode")
+    # the grouped decode reads each prompt's shared blocks once for its 8 beams
+    gs, sb, mg = shared_prefix_groups(m.decode_tables, m.decode_seq_lens, 16)
+    assert gs.tolist() == list(range(0, 129, 8)) and mg == 8
+    assert np.array_equal(sb, np.repeat(m.extra["shared_lens"] // 16, 8))
+    gout = run_decode_grouped(dec, gs, sb, mg)
+    assert_close(widen(gout), want, ATOL, RTOL, "beams grouped decode")
