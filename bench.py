@@ -69,6 +69,29 @@ def time_calls(fn, steps: int, warmup: int):
     return total / steps, total
 
 
+def time_cold(fn, reps: int, flush_mib: int = 512):
+    """Per-call times with the caches cold: before each call a `flush_mib` MiB scratch buffer is
+    overwritten, which evicts the 4 MB L2s and the 256 MB MALL, then the call is bracketed by
+    its own pair of HIP events.  The flush keeps the device busy while the host enqueues the
+    call, so the events see no launch gap.  Returns median, p10 and p90 in ms."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for i, (e0, e1) in enumerate(evs):
+        scratch.fill_(i & 0xFF)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    del scratch
+    return dict(median_ms=float(np.median(t)), p10_ms=float(np.percentile(t, 10)),
+                p90_ms=float(np.percentile(t, 90)), reps=reps)
+
+
 def copy_calibration(mib: int, steps: int = 10) -> None:
     """A plain device-to-device copy of `mib` MiB, to scale rocprofv3's FETCH_SIZE/WRITE_SIZE
     (each should read mib * 1024 KiB per dispatch)."""
@@ -145,14 +168,21 @@ def grouped_decode_callable(b, group_start, shared_blocks, max_group):
     return fn
 
 
-def bench_decode(b, steps, warmup, name):
+def bench_decode(b, steps, warmup, name, cold_reps=0):
     fn = decode_callable(b)
     mean_ms, total_ms = time_calls(fn, steps, warmup)
     nbytes = kv_bytes(b.seq_lens, b.num_kv_heads, b.head_dim)
     gbps = nbytes / (mean_ms * 1e-3) / 1e9
     log(f"{name}: {mean_ms * 1e3:.1f} us/call, "
         f"{nbytes / 1e6:.1f} MB KV -> {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of HBM)")
-    return dict(ms=mean_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps)
+    res = dict(ms=mean_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps)
+    if cold_reps:
+        c = time_cold(fn, cold_reps)
+        c["gbps_median"] = nbytes / (c["median_ms"] * 1e-3) / 1e9
+        log(f"{name} cold caches: median {c['median_ms'] * 1e3:.1f} us (p10 "
+            f"{c['p10_ms'] * 1e3:.1f}, p90 {c['p90_ms'] * 1e3:.1f}) -> {c['gbps_median']:.0f} GB/s")
+        res["cold"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in c.items()}
+    return res
 
 
 def chunk_flops(prefixes, chunk_lens, num_q_heads, head_dim) -> float:
@@ -264,6 +294,8 @@ def bench_beams(steps, warmup):
     t_cow = time_calls(cow, steps, warmup)
     t_dec = time_calls(dfn, steps, warmup)
     t_grp = time_calls(gfn, steps, warmup)
+    cold_dec = time_cold(dfn, 20)
+    cold_grp = time_cold(gfn, 20)
     logical = kv_bytes(m.decode_seq_lens, 8, 128)
     used = np.unique(np.concatenate([m.decode_tables[i, :-(-int(L) // 16)]
                                      for i, L in enumerate(m.decode_seq_lens)]))
@@ -274,11 +306,46 @@ def bench_beams(steps, warmup):
                decode_logical_gbps=logical / (t_dec[0] * 1e-3) / 1e9,
                decode_unique_gbps=unique_bytes / (t_dec[0] * 1e-3) / 1e9,
                grouped_decode_ms=t_grp[0],
-               grouped_unique_gbps=unique_bytes / (t_grp[0] * 1e-3) / 1e9)
+               grouped_unique_gbps=unique_bytes / (t_grp[0] * 1e-3) / 1e9,
+               decode_cold_median_ms=cold_dec["median_ms"],
+               grouped_decode_cold_median_ms=cold_grp["median_ms"])
     log(f"beam step: {t_step[0] * 1e3:.1f} us | cow {t_cow[0] * 1e3:.1f} us | decode "
         f"{t_dec[0] * 1e3:.1f} us, {res['decode_logical_gbps']:.0f} GB/s logical, "
         f"{res['decode_unique_gbps']:.0f} GB/s unique | grouped decode "
-        f"{t_grp[0] * 1e3:.1f} us, {res['grouped_unique_gbps']:.0f} GB/s unique")
+        f"{t_grp[0] * 1e3:.1f} us, {res['grouped_unique_gbps']:.0f} GB/s unique | cold caches: "
+        f"decode {cold_dec['median_ms'] * 1e3:.1f} us, grouped {cold_grp['median_ms'] * 1e3:.1f} us")
+    return res
+
+
+def bench_swap(steps, warmup, num_blocks=2048):
+    """Preemption by swapping: `num_blocks` whole blocks (8 kv heads x 16 x 128 bf16, K and V:
+    64 KiB each) copied device -> pinned host and back with swap_blocks, the pairs planned by the
+    native block manager (one request holding them all, swapped out then in)."""
+    from paged_kv_cache_341_amd.native_block_manager import NativeBlockManager
+    from paged_kv_cache_341_amd.block_manager import SWAP
+    nb = num_blocks + 64
+    rng = np.random.default_rng(3420)
+    bm = NativeBlockManager(nb, 16, free_order=rng.permutation(nb), num_cpu_blocks=num_blocks,
+                            cpu_free_order=rng.permutation(num_blocks))
+    bm.add_sequence(0, num_blocks * 16)
+    _, out_pairs = bm.preempt_latest(SWAP)
+    _, in_pairs = bm.swap_in_earliest()
+    shape = (nb, 8, 16, 128)
+    k = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    hk = torch.zeros((num_blocks,) + shape[1:], dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    po = i64(np.asarray(out_pairs, np.int64))
+    pi = i64(np.asarray(in_pairs, np.int64))
+    checks.check_swap_pairs(np.asarray(out_pairs), nb, num_blocks)
+    checks.check_swap_pairs(np.asarray(in_pairs), num_blocks, nb)
+    t_out = time_calls(lambda: ops.swap_blocks(hk, hv, k, v, po), steps, warmup)[0]
+    t_in = time_calls(lambda: ops.swap_blocks(k, v, hk, hv, pi), steps, warmup)[0]
+    nbytes = num_blocks * 2 * 8 * 16 * 128 * 2
+    res = dict(blocks=num_blocks, bytes=nbytes, swap_out_ms=t_out, swap_in_ms=t_in,
+               swap_out_gbps=nbytes / (t_out * 1e-3) / 1e9, swap_in_gbps=nbytes / (t_in * 1e-3) / 1e9)
+    log(f"swap {num_blocks} blocks ({nbytes / 2**20:.0f} MiB): out {t_out * 1e3:.0f} us "
+        f"({res['swap_out_gbps']:.1f} GB/s), in {t_in * 1e3:.0f} us ({res['swap_in_gbps']:.1f} GB/s)")
     return res
 
 
@@ -345,7 +412,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams")
+    ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams,swap")
     ap.add_argument("--sweep-block-size", action="store_true",
                     help="also sweep block sizes 8/16/32/64, scattered vs contiguous blocks")
     ap.add_argument("--overlap-mixed", action="store_true",
@@ -369,7 +436,7 @@ def main():
 
     log("workload decode_bf16 (64 seqs, lens U[128,4096], 32/8 heads, D128, bf16)")
     b = W.decode_bf16(device="cuda", poison=False)
-    dec = bench_decode(b, steps, warmup, "decode_bf16")
+    dec = bench_decode(b, steps, warmup, "decode_bf16", cold_reps=100)
     S, msl = b.num_seqs, int(b.seq_lens.max())
     bps_ws = ops.pa_decode_workspace_size(S, 32, 8, 128, 16, msl)
     del b
@@ -383,11 +450,14 @@ def main():
     if "long" not in skip:
         lb = W.long_bf16(device="cuda", poison=False)
         extra["long_decode"] = bench_decode(lb, max(steps // 5, 5), max(warmup // 2, 2),
-                                            "long_bf16")
+                                            "long_bf16", cold_reps=20)
         del lb
         torch.cuda.empty_cache()
     if "beams" not in skip:
         extra["beam_step"] = bench_beams(max(steps // 2, 5), warmup)
+        torch.cuda.empty_cache()
+    if "swap" not in skip:
+        extra["swap"] = bench_swap(5, 2)
         torch.cuda.empty_cache()
     if args.sweep_block_size:
         extra["block_size_sweep"] = sweep_block_size(max(steps // 2, 5), warmup)
@@ -409,6 +479,7 @@ def main():
                                "heads, head_dim 128, block_size 16, bf16 KV, fp32 accumulate",
                    "num_seqs": S, "kv_bytes_per_step": dec["kv_bytes"],
                    "workspace_bytes": bps_ws},
+        "decode_cold_caches": dec["cold"],
         "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(),

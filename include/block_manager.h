@@ -1,0 +1,139 @@
+/*
+ * block_manager.h - native host-side allocator for a paged KV pool (C ABI).
+ *
+ * What it manages, as the pages describe it:
+ *   - a pool of equal physical blocks (16 tokens by default); each sequence sees logical
+ *     blocks filled left to right and a block table maps them to physical blocks; blocks are
+ *     taken one at a time as the current one fills and a finished sequence returns them
+ *     (cloudmash "Batching and PagedAttention", section "PagedAttention", steps 1-3;
+ *     study-docs "PagedAttention & Continuous Batching", section "Block tables");
+ *   - fork shares the parent's block ids and raises their reference counts; the first write
+ *     into a shared block takes a fresh block and copies (study-docs "Copy-on-write";
+ *     cloudmash "Sharing blocks");
+ *   - when blocks run out, the most recently arrived request is preempted first and all of
+ *     its blocks go together, either swapped out to CPU memory or freed and recomputed later
+ *     from its tokens so far (cloudmash, "When blocks run out");
+ *   - capacity is counted in blocks so admission can refuse early, and the manager keeps the
+ *     counters the pages name: free and used blocks, allocation failures, tail waste,
+ *     preemptions (llmdeepdive "PagedAttention & continuous batching", section "Concept").
+ *
+ * Readings where the pages are silent (the Python BlockManager in block_manager.py follows
+ * the same ones; the two are tested against each other):
+ *   - a writer that finds a block's count above one copies it; the last holder writes in
+ *     place;
+ *   - a request is a sequence admitted with pa_bm_add_sequence plus all of its forks;
+ *     arrival order is admission order; preemption evicts a whole request;
+ *   - swap-out gives each distinct GPU block of the request one CPU block (members in request
+ *     order, blocks in table order, first appearance) and carries its reference count;
+ *     swap-in mirrors it and takes the earliest-arrived swapped request first;
+ *   - recompute frees the blocks and keeps each member's token count; after
+ *     pa_bm_resume_recompute each member re-appends its tokens into private blocks;
+ *   - free stacks: freed blocks are reused first; the initial order is given by the caller.
+ *
+ * Slots are block * block_size + offset (int64).  Copy pairs are (src, dst) block ids:
+ * copy-on-write pairs within the GPU pool, swap-out pairs (gpu, cpu), swap-in pairs
+ * (cpu, gpu); the caller runs them on the device (cow_copy_blocks, swap_blocks) before the
+ * blocks they free are written.
+ *
+ * Threading: a pa_bm is not thread-safe; calls on different managers are independent.  On
+ * failure a call changes nothing, returns a non-zero status and leaves a message for
+ * pa_bm_last_error on the calling thread.  No call allocates device memory or touches a GPU.
+ */
+#ifndef PAGED_KV_BLOCK_MANAGER_H_
+#define PAGED_KV_BLOCK_MANAGER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_bm pa_bm;
+
+typedef enum pa_bm_status {
+  PA_BM_OK = 0,
+  PA_BM_INVALID = 1,          /* bad argument: size, unknown or duplicate id, output too small */
+  PA_BM_OUT_OF_BLOCKS = 2,    /* the pool (or the CPU pool for a swap) is short */
+  PA_BM_NO_VICTIM = 3,        /* nothing to preempt or to swap in */
+  PA_BM_WRONG_STATE = 4       /* the sequence or request is not in the state the call needs */
+} pa_bm_status;
+
+typedef enum pa_bm_seq_state { PA_BM_RUNNING = 0, PA_BM_SWAPPED = 1, PA_BM_RECOMPUTE = 2 } pa_bm_seq_state;
+typedef enum pa_bm_mode { PA_BM_MODE_SWAP = 0, PA_BM_MODE_RECOMPUTE = 1 } pa_bm_mode;
+
+typedef struct pa_bm_stats {
+  int64_t num_blocks, free_blocks, num_cpu_blocks, free_cpu_blocks;
+  int64_t allocation_failures, cow_copies, blocks_allocated, blocks_freed;
+  int64_t preemptions_swap, preemptions_recompute, blocks_swapped_out, blocks_swapped_in;
+  int64_t tail_waste_slots;   /* unfilled slots in the last blocks of GPU-resident sequences */
+  int64_t num_sequences, num_requests;
+} pa_bm_stats;
+
+/* A manager over num_blocks GPU blocks and num_cpu_blocks CPU blocks (may be 0).  The free
+ * orders list the ids handed out first (index 0 first); NULL means 0, 1, 2, ...  Returns NULL
+ * on a bad argument (see pa_bm_last_error). */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t num_cpu_blocks, int32_t block_size,
+                    const int32_t* free_order, const int32_t* cpu_free_order);
+void pa_bm_destroy(pa_bm* bm);
+
+/* Admit a new sequence (a new request) holding num_tokens tokens; slots_out (may be NULL)
+ * receives their num_tokens slots.  OUT_OF_BLOCKS refuses it up front. */
+pa_bm_status pa_bm_add_sequence(pa_bm* bm, int64_t seq_id, int64_t num_tokens,
+                                int64_t* slots_out);
+
+/* Grow a resident sequence by num_new tokens: slots_out (may be NULL) receives num_new slots,
+ * cow_pairs_out receives num_cow (src, dst) pairs, at most cow_capacity (one suffices: only the
+ * block being written can be shared). */
+pa_bm_status pa_bm_append(pa_bm* bm, int64_t seq_id, int64_t num_new, int64_t* slots_out,
+                          int64_t* cow_pairs_out, int32_t cow_capacity, int32_t* num_cow);
+
+pa_bm_status pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+pa_bm_status pa_bm_free(pa_bm* bm, int64_t seq_id);
+
+/* Free GPU blocks an append of num_new tokens would take (new blocks plus a copy), or -1. */
+int64_t pa_bm_blocks_needed(const pa_bm* bm, int64_t seq_id, int64_t num_new);
+
+/* length, number of blocks, state, request id and tokens awaiting recompute (NULLs allowed) */
+pa_bm_status pa_bm_seq_info(const pa_bm* bm, int64_t seq_id, int64_t* length,
+                            int32_t* num_blocks, int32_t* state, int64_t* request,
+                            int64_t* recompute_tokens);
+
+/* The sequence's block ids (CPU ids while swapped) into out[capacity]. */
+pa_bm_status pa_bm_table(const pa_bm* bm, int64_t seq_id, int32_t* out, int32_t capacity);
+
+/* int32 [n][width] tables of the given sequences, -1 past each one's blocks. */
+pa_bm_status pa_bm_block_tables(const pa_bm* bm, const int64_t* seq_ids, int32_t n,
+                                int32_t width, int32_t* out);
+
+/* Reference count of a GPU (on_cpu = 0) or CPU block; -1 for an id out of range. */
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block, int32_t on_cpu);
+
+/* Preempt the most recently arrived running request other than `protect_request` (-1: none).
+ * SWAP: pairs_out receives (gpu, cpu) pairs, num_pairs of them (capacity: at most the
+ * request's block count).  RECOMPUTE: no pairs.  NO_VICTIM if there is none; OUT_OF_BLOCKS
+ * (nothing changed) if the CPU pool cannot take the swap; INVALID if capacity is short. */
+pa_bm_status pa_bm_preempt_latest(pa_bm* bm, int32_t mode, int64_t protect_request,
+                                  int64_t* request_out, int64_t* pairs_out, int32_t capacity,
+                                  int32_t* num_pairs);
+
+/* Swap the earliest-arrived swapped request back in: (cpu, gpu) pairs. */
+pa_bm_status pa_bm_swap_in_earliest(pa_bm* bm, int64_t* request_out, int64_t* pairs_out,
+                                    int32_t capacity, int32_t* num_pairs);
+
+/* Make a recompute-preempted request resident (empty); its members' token counts stay readable
+ * through pa_bm_seq_info until they are re-appended by the caller. */
+pa_bm_status pa_bm_resume_recompute(pa_bm* bm, int64_t request);
+
+/* Members of a request, in request order, into out[capacity]; *count receives their number. */
+pa_bm_status pa_bm_request_members(const pa_bm* bm, int64_t request, int64_t* out,
+                                   int32_t capacity, int32_t* count);
+
+pa_bm_status pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
+const char* pa_bm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* PAGED_KV_BLOCK_MANAGER_H_ */

@@ -189,6 +189,29 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
                           int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * swap_blocks - whole-block copies between two pools, for preemption by swapping: a preempted
+ * request's blocks are swapped out to CPU memory and back in later, all of a sequence's blocks
+ * together (cloudmash "Batching and PagedAttention", section "When blocks run out").  For each
+ * pair p:
+ *   dst_k[pairs[p][1]] = src_k[pairs[p][0]]; dst_v[pairs[p][1]] = src_v[pairs[p][0]]
+ * whole blocks, exact bit copies.  Both pools have the layout of the device pool
+ * ([blocks][num_kv_heads][block_size][head_dim]); either may be host memory that the device
+ * can map (pinned with hipHostMalloc), the other device memory: swap-out copies device to host,
+ * swap-in host to device.  The pairs come from pa_bm_preempt_latest / pa_bm_swap_in_earliest
+ * (block_manager.h) and live in device or mapped host memory.
+ *
+ *   block_pairs  [num_pairs][2] int64 (src block, dst block); num_pairs == 0 is a no-op
+ *
+ * Preconditions (not checked on the device; checks.check_swap_pairs checks them on the host):
+ * src ids in [0, num_src_blocks), dst ids in [0, num_dst_blocks), dst ids distinct.  The
+ * source and destination pools must be different allocations.
+ */
+pa_status swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                      const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_src_blocks,
+                      int32_t num_dst_blocks, pa_dtype dtype, void* stream);
+
+/*
  * pa_hbm_read_probe - a diagnostic, not part of the paged path: reads `bytes` of device memory
  * at `src` with 16-byte non-temporal loads (the load the decode kernel streams KV with) on
  * `num_workgroups` workgroups of 256 lanes, and writes one XOR-folded word per lane to `sink`

@@ -24,6 +24,10 @@ What it computes is the plain definition, evaluated through the block table:
     padding (study-docs "Block tables": a sequence grows into its current block).
   * Copy-on-write: the whole destination block becomes a byte copy of the source block, K and V
     (study-docs "Copy-on-write"; cloudmash "Sharing blocks").
+  * Swap: a preempted request's blocks move to CPU memory and back, whole blocks, all of a
+    sequence's blocks together (cloudmash "Batching and PagedAttention", "When blocks run out");
+    a swap is a byte copy of each source block of one pool into its destination block of the
+    other pool.
 
 Readings taken where the pages are silent: the pool layout is [blocks, kv_heads, B, head_dim];
 query head h reads kv head h // (Hq / Hkv); seq_lens count the tokens appended in the same step
@@ -235,3 +239,21 @@ def cow_ref(k_cache, v_cache, pairs):
         kc[dst] = k_cache[src]
         vc[dst] = v_cache[src]
     return kc, vc
+
+
+def swap_ref(dst_k, dst_v, src_k, src_v, pairs):
+    """New (dst_k, dst_v): destination block pairs[p][1] becomes a byte copy of source block
+    pairs[p][0] of the other pool (K and V); no other destination block changes.  Destination
+    ids must be distinct and every id in range."""
+    dk = np.array(dst_k, copy=True)
+    dv = np.array(dst_v, copy=True)
+    p = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if p.size and (p.min() < 0 or p[:, 0].max() >= src_k.shape[0]
+                   or p[:, 1].max() >= dk.shape[0]):
+        raise OracleInputError("swap block id out of range")
+    if np.unique(p[:, 1]).size != p.shape[0]:
+        raise OracleInputError("duplicate swap destination")
+    for src, dst in p:
+        dk[dst] = src_k[src]
+        dv[dst] = src_v[src]
+    return dk, dv

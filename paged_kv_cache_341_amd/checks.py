@@ -81,3 +81,15 @@ def check_pairs(pairs: np.ndarray, num_blocks: int) -> None:
         raise ValueError("duplicate destination")
     if np.intersect1d(p[:, 0], p[:, 1]).size:
         raise ValueError("a destination is also a source")
+
+
+def check_swap_pairs(pairs: np.ndarray, num_src_blocks: int, num_dst_blocks: int) -> None:
+    p = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if p.size == 0:
+        return
+    if p[:, 0].min() < 0 or p[:, 0].max() >= num_src_blocks:
+        raise ValueError("source block id out of range")
+    if p[:, 1].min() < 0 or p[:, 1].max() >= num_dst_blocks:
+        raise ValueError("destination block id out of range")
+    if np.unique(p[:, 1]).size != p.shape[0]:
+        raise ValueError("duplicate destination")

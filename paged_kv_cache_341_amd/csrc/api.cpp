@@ -452,13 +452,47 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
   if (block_bytes % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "cow_copy_blocks: block bytes must be a multiple of 16");
   pa::CowArgs a{};
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.dst_k = k_cache;
+  a.dst_v = v_cache;
+  a.src_k = k_cache;
+  a.src_v = v_cache;
   a.pairs = block_pairs;
   a.num_pairs = num_pairs;
   a.block_bytes = block_bytes;
   a.stream = static_cast<hipStream_t>(stream);
   return device_status(pa::launch_cow(a), "cow_copy_blocks launch");
+}
+
+pa_status swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                      const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_src_blocks,
+                      int32_t num_dst_blocks, pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_src_blocks <= 0 || num_dst_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "swap_blocks: sizes must be positive (num_pairs >= 0)");
+  if (!valid_dtype(dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "swap_blocks: unknown dtype");
+  if (num_pairs == 0) return ok();
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs)
+    return fail(PA_ERR_INVALID_ARGUMENT, "swap_blocks: null pointer argument");
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v))
+    return fail(PA_ERR_INVALID_ARGUMENT, "swap_blocks: pools must be 16-byte aligned");
+  if (dst_k == src_k || dst_v == src_v)
+    return fail(PA_ERR_INVALID_ARGUMENT, "swap_blocks: source and destination pools are the "
+                "same (use cow_copy_blocks)");
+  const int64_t block_bytes =
+      static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "swap_blocks: block bytes must be a multiple of 16");
+  pa::CowArgs a{};
+  a.dst_k = dst_k;
+  a.dst_v = dst_v;
+  a.src_k = src_k;
+  a.src_v = src_v;
+  a.pairs = block_pairs;
+  a.num_pairs = num_pairs;
+  a.block_bytes = block_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+  return device_status(pa::launch_cow(a), "swap_blocks launch");
 }
 
 pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,

@@ -38,10 +38,14 @@ __global__ __launch_bounds__(kCopyThreads) void kv_append_kernel(
   }
 }
 
-// One lane per 16-byte chunk of a block, for K and V.
-__global__ __launch_bounds__(kCopyThreads) void cow_copy_kernel(
-    char* __restrict__ k_cache, char* __restrict__ v_cache, const int64_t* __restrict__ pairs,
-    int64_t total_chunks, int64_t chunks_per_block) {
+// One lane per 16-byte chunk of a block, for K and V: block pairs[p][1] of the destination
+// pools becomes a copy of block pairs[p][0] of the source pools.  Copy-on-write passes the same
+// pool as source and destination (a destination is never a source there, so the blocks read
+// and written are distinct); a swap passes a device pool and a host pool the device can map.
+__global__ __launch_bounds__(kCopyThreads) void block_copy_kernel(
+    char* __restrict__ dst_k, char* __restrict__ dst_v, const char* __restrict__ src_k,
+    const char* __restrict__ src_v, const int64_t* __restrict__ pairs, int64_t total_chunks,
+    int64_t chunks_per_block) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
        i < total_chunks; i += stride) {
@@ -51,8 +55,8 @@ __global__ __launch_bounds__(kCopyThreads) void cow_copy_kernel(
     const int64_t dst = pairs[2 * p + 1];
     const int64_t so = (src * chunks_per_block + c) * 16;
     const int64_t d = (dst * chunks_per_block + c) * 16;
-    store16(k_cache + d, load16(k_cache + so));
-    store16(v_cache + d, load16(v_cache + so));
+    store16(dst_k + d, load16(src_k + so));
+    store16(dst_v + d, load16(src_v + so));
   }
 }
 
@@ -76,9 +80,10 @@ hipError_t launch_cow(const CowArgs& a) {
   const int64_t per_block = a.block_bytes / 16;
   const int64_t total = per_block * a.num_pairs;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(cow_copy_kernel, dim3(grid_for(total)), dim3(kCopyThreads), 0, a.stream,
-                     static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache), a.pairs, total,
-                     per_block);
+  hipLaunchKernelGGL(block_copy_kernel, dim3(grid_for(total)), dim3(kCopyThreads), 0, a.stream,
+                     static_cast<char*>(a.dst_k), static_cast<char*>(a.dst_v),
+                     static_cast<const char*>(a.src_k), static_cast<const char*>(a.src_v),
+                     a.pairs, total, per_block);
   return hipGetLastError();
 }
 

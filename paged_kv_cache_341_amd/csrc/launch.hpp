@@ -53,9 +53,13 @@ struct AppendArgs {
   hipStream_t stream;
 };
 
+// Whole-block copies from (src_k, src_v) to (dst_k, dst_v): copy-on-write within one pool, or
+// swap between a device pool and a mapped host pool.
 struct CowArgs {
-  void* k_cache;
-  void* v_cache;
+  void* dst_k;
+  void* dst_v;
+  const void* src_k;
+  const void* src_v;
   const int64_t* pairs;
   int num_pairs;
   int64_t block_bytes;

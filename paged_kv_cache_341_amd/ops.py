@@ -26,7 +26,13 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED
 EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_grouped",
             "pa_decode_grouped_workspace_size", "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
-            "pa_last_error", "pa_hbm_read_probe")
+            "pa_last_error", "pa_hbm_read_probe", "swap_blocks")
+# the native block manager (include/block_manager.h), bound in native_block_manager.py
+BM_EXPORTED = ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append",
+               "pa_bm_fork", "pa_bm_free", "pa_bm_blocks_needed", "pa_bm_seq_info",
+               "pa_bm_table", "pa_bm_block_tables", "pa_bm_refcount", "pa_bm_preempt_latest",
+               "pa_bm_swap_in_earliest", "pa_bm_resume_recompute", "pa_bm_request_members",
+               "pa_bm_get_stats", "pa_bm_last_error")
 
 
 class PagedAttnError(RuntimeError):
@@ -72,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     _vp]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.swap_blocks.restype = ctypes.c_int
+    lib.swap_blocks.argtypes = [_vp] * 5 + [_i32] * 6 + [ctypes.c_int, _vp]
     lib.pa_hbm_read_probe.restype = ctypes.c_int
     lib.pa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -236,6 +244,29 @@ def cow_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: t
     P = block_pairs.shape[0]
     st = lib.cow_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), P, Hkv, D, B, NB,
                              _dtype_code(k_cache), _stream(k_cache, stream))
+    _check(st)
+
+
+def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                src_v: torch.Tensor, block_pairs: torch.Tensor, stream=None) -> None:
+    """dst[pairs[p][1]] = src[pairs[p][0]] (K and V) between a device pool and a pinned host
+    pool, either direction (see pagedattn.h); enqueued on the device pool's stream."""
+    lib = load_library()
+    _contig(dst_k, dst_v, src_k, src_v, block_pairs)
+    _need(block_pairs.dtype == torch.int64, "block_pairs must be int64 [P, 2]")
+    _need(tuple(dst_k.shape[1:]) == tuple(src_k.shape[1:]) and dst_k.shape == dst_v.shape
+          and src_k.shape == src_v.shape, "pool shapes differ")
+    _need(dst_k.dtype == src_k.dtype == dst_v.dtype == src_v.dtype, "dtypes must match")
+    dev = dst_k if dst_k.is_cuda else src_k
+    host = src_k if dst_k.is_cuda else dst_k
+    _need(dev.is_cuda and (host.is_cuda or host.is_pinned()),
+          "one pool must be on the device and the other on the device or in pinned host memory")
+    _need(block_pairs.is_cuda or block_pairs.is_pinned(),
+          "block_pairs must be device or pinned host memory")
+    _, Hkv, B, D = dst_k.shape
+    st = lib.swap_blocks(_ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v), _ptr(block_pairs),
+                         block_pairs.shape[0], Hkv, D, B, src_k.shape[0], dst_k.shape[0],
+                         _dtype_code(dev), _stream(dev, stream))
     _check(st)
 
 

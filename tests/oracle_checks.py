@@ -292,6 +292,33 @@ def check_cow(ref):
         raise AssertionError(f"bad pairs accepted: {bad}")
 
 
+def check_swap(ref):
+    """A swap-out and swap-in round trip through a smaller second pool restores every swapped
+    block byte for byte in its new place, leaves the rest alone, and refuses bad pairs."""
+    rng = _rng(127)
+    gk = rng.standard_normal((8, 2, 4, 3)).astype(np.float32)
+    gv = rng.standard_normal((8, 2, 4, 3)).astype(np.float32)
+    ck = np.full((5, 2, 4, 3), np.nan, np.float32)
+    cv = np.full((5, 2, 4, 3), np.nan, np.float32)
+    out = np.array([[6, 3], [1, 0], [4, 4]], np.int64)        # (gpu, cpu)
+    ck2, cv2 = ref.swap_ref(ck, cv, gk, gv, out)
+    assert ck2[3].tobytes() == gk[6].tobytes() and cv2[0].tobytes() == gv[1].tobytes()
+    assert np.all(np.isnan(ck2[[1, 2]])) and np.all(np.isnan(cv2[[1, 2]]))
+    back = np.array([[3, 2], [0, 7], [4, 5]], np.int64)       # (cpu, gpu), new places
+    gk2, gv2 = ref.swap_ref(gk, gv, ck2, cv2, back)
+    for (g, c), (c2, g2) in zip(out, back):
+        assert c == c2 and gk2[g2].tobytes() == gk[g].tobytes()
+        assert gv2[g2].tobytes() == gv[g].tobytes()
+    keep = [b for b in range(8) if b not in (2, 7, 5)]
+    assert np.array_equal(gk2[keep], gk[keep]) and np.array_equal(gv2[keep], gv[keep])
+    for bad in ([[0, 5]], [[8, 0]], [[1, 2], [3, 2]], [[-1, 0]]):
+        try:
+            ref.swap_ref(ck, cv, gk, gv, np.array(bad, np.int64))
+        except ref.OracleInputError:
+            continue
+        raise AssertionError(f"bad pairs accepted: {bad}")
+
+
 def check_nan_poison(ref):
     """NaN in every slot no sequence owns leaves the output finite and unchanged (S13)."""
     t = Tiny([5, 16, 30], Hq=2, Hkv=1, D=8, block_size=16, seed=131)
@@ -333,5 +360,6 @@ def check_bf16_decode(ref):
 ALL_CHECKS = [check_hand_example, check_brute_force, check_permutation,
               check_block_size_invariance, check_row_sums, check_single_token, check_zero_query,
               check_constant_values, check_needle, check_sdpa, check_chunk_positions,
-              check_append_roundtrip, check_cow, check_nan_poison, check_bf16_widening,
+              check_append_roundtrip, check_cow, check_swap, check_nan_poison,
+              check_bf16_widening,
               check_bf16_decode]

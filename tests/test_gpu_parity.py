@@ -10,9 +10,10 @@ import torch
 
 from oracle import paged_ref as ref
 from paged_kv_cache_341_amd import workloads as W
-from paged_kv_cache_341_amd import ops
+from paged_kv_cache_341_amd import checks, ops
 from paged_kv_cache_341_amd.block_manager import shared_prefix_groups
-from tests.gpu_util import (ATOL, F32_ATOL, F32_RTOL, RTOL, assert_close, compact, dev_i32, raw,
+from tests.gpu_util import (ATOL, F32_ATOL, F32_RTOL, RTOL, assert_close, compact, dev_i32,
+                            dev_i64, raw,
                             run_append, run_cow, run_decode, run_decode_grouped, run_prefill, say,
                             widen)
 
@@ -368,3 +369,67 @@ def test_beam_step_full_size():
     assert np.array_equal(sb, np.repeat(m.extra["shared_lens"] // 16, 8))
     gout = run_decode_grouped(dec, gs, sb, mg)
     assert_close(widen(gout), want, ATOL, RTOL, "beams grouped decode")
+
+
+# ------------------------------------------------------------------------------ swap
+def test_swap_out_and_in_through_pinned_host_pool():
+    """The native block manager preempts the two latest requests by swapping: their blocks go
+    to a pinned host pool (device-to-host swap_blocks), the freed device blocks are reused and
+    overwritten, then both come back into new device blocks.  Host and device pools match the
+    oracle's byte for byte after each step, and decode over the restored tables gives the same
+    bits as before the swap."""
+    from paged_kv_cache_341_amd.native_block_manager import NativeBlockManager
+    from paged_kv_cache_341_amd.block_manager import SWAP
+    say("case: swap out / in of two requests through a pinned host pool")
+    rng = np.random.default_rng(1900)
+    NB, NC, Hkv, D = 64, 40, 2, 128
+    bm = NativeBlockManager(NB, 16, free_order=rng.permutation(NB), num_cpu_blocks=NC,
+                            cpu_free_order=rng.permutation(NC))
+    bm.add_sequence(0, 100)
+    bm.add_sequence(1, 70)
+    bm.fork(1, 2)
+    _, cow = bm.append_tokens(2, 5)
+    bm.add_sequence(3, 200)
+    g = torch.Generator(device=DEV).manual_seed(1900)
+    k = torch.randn((NB, Hkv, 16, D), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((NB, Hkv, 16, D), generator=g, device=DEV).to(torch.bfloat16)
+    run_cow(k, v, np.asarray(cow, np.int64))
+    seqs = [0, 1, 2, 3]
+    q = torch.randn((4, 8, D), generator=g, device=DEV).to(torch.bfloat16)
+
+    def decode():
+        b = W.DecodeBatch(q=q, k_cache=k, v_cache=v, block_tables=bm.block_tables(seqs),
+                          seq_lens=np.array([bm.seq_len(s) for s in seqs], np.int32),
+                          scale=W.default_scale(D), num_q_heads=8, num_kv_heads=Hkv,
+                          head_dim=D, block_size=16, dtype="bf16")
+        return run_decode(b)
+
+    before = decode()
+    hk = torch.full((NC, Hkv, 16, D), float("nan"), dtype=torch.bfloat16).pin_memory()
+    hv = torch.full((NC, Hkv, 16, D), float("nan"), dtype=torch.bfloat16).pin_memory()
+    want_hk, want_hv = raw(hk), raw(hv)
+    for expect in (2, 1):
+        r, pairs = bm.preempt_latest(SWAP)
+        assert r == expect
+        p = np.asarray(pairs, np.int64)
+        checks.check_swap_pairs(p, NB, NC)
+        gk, gv = raw(k), raw(v)
+        ops.swap_blocks(hk, hv, k, v, dev_i64(p))
+        torch.cuda.synchronize()
+        want_hk, want_hv = ref.swap_ref(want_hk, want_hv, gk, gv, p)
+        assert np.array_equal(raw(hk), want_hk) and np.array_equal(raw(hv), want_hv)
+    # the freed device blocks are reused: overwrite them
+    freed = [b for b in range(NB) if bm.refcount(b) == 0]
+    k[freed] = float("nan")
+    v[freed] = float("nan")
+    for expect in (1, 2):
+        r, pairs = bm.swap_in_earliest()
+        assert r == expect
+        p = np.asarray(pairs, np.int64)
+        checks.check_swap_pairs(p, NC, NB)
+        gk, gv = raw(k), raw(v)
+        ops.swap_blocks(k, v, hk, hv, dev_i64(p))
+        torch.cuda.synchronize()
+        wk, wv = ref.swap_ref(gk, gv, raw(hk), raw(hv), p)
+        assert np.array_equal(raw(k), wk) and np.array_equal(raw(v), wv)
+    assert torch.equal(decode(), before)

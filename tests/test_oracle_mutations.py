@@ -9,6 +9,7 @@ _orig_attend = paged_ref.attend
 _orig_softmax = paged_ref.softmax_weights
 _orig_append = paged_ref.append_ref
 _orig_cow = paged_ref.cow_ref
+_orig_swap = paged_ref.swap_ref
 _orig_gather = paged_ref.gather_tokens
 
 
@@ -36,6 +37,9 @@ MUTATIONS = {
     "append_skips_last": ("append_ref", lambda kc, vc, kn, vn, sm, B=16:
                           _orig_append(kc, vc, kn, vn, np.where(np.arange(len(sm)) == len(sm) - 1, -1, sm), B)),
     "cow_k_only": ("cow_ref", lambda kc, vc, p: (_orig_cow(kc, vc, p)[0], np.array(vc, copy=True))),
+    "swap_pairs_reversed": ("swap_ref", lambda dk, dv, sk, sv, p:
+                            _orig_swap(dk, dv, sk, sv, np.asarray(p)[:, ::-1])),
+    "swap_v_from_k": ("swap_ref", lambda dk, dv, sk, sv, p: _orig_swap(dk, dv, sk, sk, p)),
 }
 
 
