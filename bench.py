@@ -239,7 +239,24 @@ def bench_mixed(steps, warmup, overlap=False):
         chunks_done.record(side)
         main.wait_event(chunks_done)
 
+    # The same iteration as one pa_mixed_step call: append, then chunks and decode splits in
+    # one persistent launch, then the decode merge.
+    dmsl = int(m.decode_seq_lens.max())
+    dt, dl = i32(m.decode_tables), i32(m.decode_seq_lens)
+    checks.check_tables(m.decode_tables, m.decode_seq_lens, nb, 16, dmsl)
+    dout = torch.empty_like(m.q_decode)
+    mws = torch.empty(ops.pa_mixed_workspace_size(192, 32, 8, 128, 16, dmsl), dtype=torch.uint8,
+                      device="cuda")
+
+    def single():
+        ops.pa_mixed_step(m.k_cache, m.v_cache, m.scale, k_new=m.k_new, v_new=m.v_new,
+                          slot_mapping=sm, chunk_out=cout, chunk_q=m.q_chunk, chunk_tables=ct,
+                          chunk_seq_lens=cl, query_start_loc=qsl, chunk_max_q_len=max_q,
+                          chunk_max_seq_len=msl_c, dec_out=dout, dec_q=m.q_decode,
+                          dec_tables=dt, dec_seq_lens=dl, dec_max_seq_len=dmsl, workspace=mws)
+
     t_step = time_calls(step, steps, warmup)
+    t_single = time_calls(single, steps, warmup)
     t_over = time_calls(step_overlapped, steps, warmup) if overlap else None
     t_app = time_calls(append, steps, warmup)
     t_pre = time_calls(prefill, steps, warmup)
@@ -256,7 +273,8 @@ def bench_mixed(steps, warmup, overlap=False):
         prefill_ms=t_pre[0], prefill_gflop=flops / 1e9, prefill_tflops=tflops,
         prefill_mfma_frac=tflops / BF16_PEAK_TFLOPS,
         decode_ms=t_dec[0], decode_kv_bytes=dec_bytes,
-        decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9)
+        decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9,
+        single_launch_ms=t_single[0], single_launch_tokens_per_s=T / (t_single[0] * 1e-3))
     if t_over is not None:
         res.update(overlapped_tokens_per_s=T / (t_over[0] * 1e-3), overlapped_ms_per_step=t_over[0])
         log(f"mixed step, chunks and decodes on two streams: {t_over[0] * 1e3:.1f} us -> "
@@ -265,6 +283,8 @@ def bench_mixed(steps, warmup, overlap=False):
         f"{t_app[0] * 1e3:.1f} us | prefill {t_pre[0] * 1e3:.1f} us {tflops:.0f} TFLOP/s "
         f"({100 * res['prefill_mfma_frac']:.1f}% MFMA) | decode {t_dec[0] * 1e3:.1f} us "
         f"{res['decode_gbps']:.0f} GB/s")
+    log(f"mixed step as one pa_mixed_step call (single launch): {t_single[0] * 1e3:.1f} us -> "
+        f"{res['single_launch_tokens_per_s']:.0f} tok/s")
     return res
 
 

@@ -189,6 +189,65 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
                           int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * pa_mixed_step - one continuous-batching iteration's attention work in a single persistent
+ * launch: the KV append of the iteration's new tokens, then the chunked-prefill rows and the
+ * decode rows together (cloudmash "Batching and PagedAttention", section "Continuous
+ * batching": prompt chunks and decode steps share an iteration, long prompts cut into chunks;
+ * llmdeepdive "Concept", continuous-batching paragraph).  Results equal kv_append followed by
+ * pa_prefill_chunk on the chunk fields and pa_decode on the decode fields (up to fp32
+ * summation order in the decodes).  Chunk rows are bound by the matrix cores and decode rows
+ * by HBM; one kernel runs both at once, one workgroup per CU, each taking work from a queue of
+ * chunk tiles (longest chunk first) and a queue of decode splits.  Enqueues three launches
+ * (append, the mixed kernel, the decode merge), no host synchronisation.
+ *
+ * Fields (pa_mixed_batch): the append's k_new, v_new [num_new_tokens][num_kv_heads][head_dim]
+ * and slot_mapping (as kv_append; num_new_tokens may be 0); the chunks' out, q, tables,
+ * seq_lens, query_start_loc and host bounds (as pa_prefill_chunk; num_chunks may be 0); the
+ * decodes' out, q, tables, seq_lens and host bounds (as pa_decode; num_seqs may be 0); the pool
+ * and head counts shared by both.  Workspace: pa_mixed_workspace_size(...) bytes, contents need
+ * no initialisation; the call uses its first 256 bytes as work counters and the rest as the
+ * decode split partials.
+ *
+ * Supported: dtype BF16, head_dim 128, block_size 16, num_q_heads/num_kv_heads in
+ * {1, 2, 4, 8}, at most 128 chunks and 2048 decode sequences.  Device-content preconditions
+ * are those of the three calls it replaces.
+ */
+typedef struct pa_mixed_batch {
+  /* append */
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+  int32_t num_new_tokens;
+  /* chunked prefill */
+  void* chunk_out;
+  const void* chunk_q;
+  const int32_t* chunk_tables;
+  const int32_t* chunk_seq_lens;
+  const int32_t* query_start_loc;
+  int32_t num_chunks, chunk_total_q, chunk_max_q_len, chunk_max_seq_len;
+  int32_t chunk_max_blocks_per_seq;
+  /* decode */
+  void* dec_out;
+  const void* dec_q;
+  const int32_t* dec_tables;
+  const int32_t* dec_seq_lens;
+  int32_t num_seqs, dec_max_seq_len, dec_max_blocks_per_seq;
+  /* pool */
+  void* k_cache;
+  void* v_cache;
+  int32_t num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  float scale;
+  pa_dtype dtype;
+} pa_mixed_batch;
+
+pa_status pa_mixed_step(const pa_mixed_batch* batch, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Bytes of workspace pa_mixed_step needs (0 for unsupported sizes). */
+size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t dec_max_seq_len);
+
+/*
  * swap_blocks - whole-block copies between two pools, for preemption by swapping: a preempted
  * request's blocks are swapped out to CPU memory and back in later, all of a sequence's blocks
  * together (cloudmash "Batching and PagedAttention", section "When blocks run out").  For each

@@ -341,6 +341,189 @@ pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const
 
 size_t pa_prefill_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
 
+// ------------------------------------------------------------------------- mixed step
+namespace {
+
+constexpr size_t kMixedHeader = 256;     // work counters
+constexpr int kMixedMaxChunks = 128;
+constexpr int kMixedMaxSeqs = 2048;
+
+struct MixedPlan {
+  int bps, nsplit;
+  size_t ml_bytes, total;
+};
+
+MixedPlan plan_mixed(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                     int block_size, int dec_max_seq_len) {
+  MixedPlan p{};
+  if (num_seqs <= 0) {
+    p.bps = 1;
+    p.nsplit = 1;
+    p.total = kMixedHeader;
+    return p;
+  }
+  const int g = num_q_heads / num_kv_heads;
+  p.bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, dec_max_seq_len);
+  const int nblk = (dec_max_seq_len + block_size - 1) / block_size;
+  p.nsplit = (nblk + p.bps - 1) / p.bps;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.nsplit;
+  p.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+  p.total = kMixedHeader + (p.nsplit > 1 ? p.ml_bytes + rows * head_dim * sizeof(float) : 0);
+  return p;
+}
+
+}  // namespace
+
+size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t dec_max_seq_len) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != 128 ||
+      block_size != kSupportedBlock || num_q_heads % num_kv_heads != 0 ||
+      (num_seqs > 0 && dec_max_seq_len <= 0))
+    return 0;
+  return plan_mixed(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dec_max_seq_len)
+      .total;
+}
+
+pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!b) return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: null batch");
+  if (b->num_new_tokens < 0 || b->num_chunks < 0 || b->num_seqs < 0 || b->num_q_heads <= 0 ||
+      b->num_kv_heads <= 0 || b->head_dim <= 0 || b->block_size <= 0 || b->num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: sizes must be positive (counts >= 0)");
+  if (b->num_q_heads % b->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: num_q_heads %d not a multiple of "
+                "num_kv_heads %d", b->num_q_heads, b->num_kv_heads);
+  if (!valid_dtype(b->dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: unknown dtype");
+  if (!b->k_cache || !b->v_cache || !aligned16(b->k_cache) || !aligned16(b->v_cache))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: pools must be non-null and 16-byte "
+                "aligned");
+  if (!(b->scale > 0.f) || b->scale == __builtin_inff())
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: scale must be finite and positive");
+  if (b->num_new_tokens > 0 &&
+      (!b->k_new || !b->v_new || !b->slot_mapping || !aligned16(b->k_new) || !aligned16(b->v_new)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: append buffers null or misaligned");
+  if (b->num_chunks > 0) {
+    if (!b->chunk_out || !b->chunk_q || !b->chunk_tables || !b->chunk_seq_lens ||
+        !b->query_start_loc || !aligned16(b->chunk_out) || !aligned16(b->chunk_q))
+      return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: chunk buffers null or misaligned");
+    if (b->chunk_total_q <= 0 || b->chunk_max_q_len <= 0 || b->chunk_max_seq_len <= 0 ||
+        b->chunk_max_blocks_per_seq <= 0 || b->chunk_max_q_len > b->chunk_total_q ||
+        b->chunk_max_q_len > b->chunk_max_seq_len ||
+        static_cast<int64_t>(b->chunk_max_seq_len) >
+            static_cast<int64_t>(b->chunk_max_blocks_per_seq) * b->block_size)
+      return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: inconsistent chunk bounds");
+  }
+  if (b->num_seqs > 0) {
+    if (!b->dec_out || !b->dec_q || !b->dec_tables || !b->dec_seq_lens ||
+        !aligned16(b->dec_out) || !aligned16(b->dec_q))
+      return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: decode buffers null or misaligned");
+    if (b->dec_max_seq_len <= 0 || b->dec_max_blocks_per_seq <= 0 ||
+        static_cast<int64_t>(b->dec_max_seq_len) >
+            static_cast<int64_t>(b->dec_max_blocks_per_seq) * b->block_size)
+      return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: inconsistent decode bounds");
+  }
+  if (b->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: only bf16 is supported");
+  if (b->head_dim != 128 || b->block_size != kSupportedBlock)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: head_dim %d, block_size %d (supported: "
+                "128, 16)", b->head_dim, b->block_size);
+  const int g = b->num_q_heads / b->num_kv_heads;
+  if (!supported_group(g))
+    return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: %d query heads per kv head (supported: "
+                "1,2,4,8)", g);
+  if (b->num_chunks > kMixedMaxChunks || b->num_seqs > kMixedMaxSeqs)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: %d chunks, %d decode sequences (at most %d "
+                "and %d)", b->num_chunks, b->num_seqs, kMixedMaxChunks, kMixedMaxSeqs);
+  const MixedPlan p = plan_mixed(b->num_seqs, b->num_q_heads, b->num_kv_heads, b->head_dim,
+                                 b->block_size, b->dec_max_seq_len);
+  if (!workspace || workspace_bytes < p.total)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_mixed_step: workspace %zu bytes, need %zu",
+                workspace_bytes, p.total);
+  if (!aligned16(workspace))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mixed_step: workspace must be 16-byte aligned");
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return fail(PA_ERR_DEVICE, "pa_mixed_step: cannot read the device's compute-unit count");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* queues = static_cast<int*>(workspace);
+  char* ws = static_cast<char*>(workspace) + kMixedHeader;
+  float* ws_ml = reinterpret_cast<float*>(ws);
+  float* ws_acc = reinterpret_cast<float*>(ws + p.ml_bytes);
+
+  // 1. append, which also zeroes the two work counters
+  pa::AppendArgs ap{};
+  ap.k_cache = b->k_cache;
+  ap.v_cache = b->v_cache;
+  ap.k_new = b->k_new;
+  ap.v_new = b->v_new;
+  ap.slot_mapping = b->slot_mapping;
+  ap.num_tokens = b->num_new_tokens;
+  ap.num_kv_heads = b->num_kv_heads;
+  ap.head_dim = b->head_dim;
+  ap.block_size = b->block_size;
+  ap.elem_bytes = 2;
+  ap.zero_words = queues;
+  ap.num_zero_words = 2;
+  ap.stream = st;
+  hipError_t e = pa::launch_append(ap);
+  if (e != hipSuccess) return device_status(e, "pa_mixed_step append launch");
+  if (b->num_chunks == 0 && b->num_seqs == 0) return ok();
+
+  // 2. chunks and decode splits in one launch
+  pa::MixedArgs m{};
+  m.chunk_out = b->chunk_out;
+  m.chunk_q = b->chunk_q;
+  m.chunk_tables = b->chunk_tables;
+  m.chunk_seq_lens = b->chunk_seq_lens;
+  m.query_start_loc = b->query_start_loc;
+  m.num_chunks = b->num_chunks;
+  m.chunk_max_blocks_per_seq = b->chunk_max_blocks_per_seq;
+  m.dec_out = b->dec_out;
+  m.dec_q = b->dec_q;
+  m.dec_tables = b->dec_tables;
+  m.dec_seq_lens = b->dec_seq_lens;
+  m.num_seqs = b->num_seqs;
+  m.dec_max_blocks_per_seq = b->dec_max_blocks_per_seq;
+  m.bps = p.bps;
+  m.nsplit_max = p.nsplit;
+  m.ws_ml = ws_ml;
+  m.ws_acc = ws_acc;
+  m.queues = queues;
+  m.k_cache = b->k_cache;
+  m.v_cache = b->v_cache;
+  m.num_q_heads = b->num_q_heads;
+  m.num_kv_heads = b->num_kv_heads;
+  m.num_workgroups = cus;
+  m.scale_log2 = b->scale * 1.4426950408889634f;
+  m.stream = st;
+  e = pa::launch_mixed(m);
+  if (e != hipSuccess) return device_status(e, "pa_mixed_step mixed launch");
+  if (b->num_seqs == 0 || p.nsplit <= 1) return ok();
+
+  // 3. merge of the decode splits
+  pa::DecodeArgs d{};
+  d.out = b->dec_out;
+  d.ws_ml = ws_ml;
+  d.ws_acc = ws_acc;
+  d.seq_lens = b->dec_seq_lens;
+  d.num_seqs = b->num_seqs;
+  d.num_q_heads = b->num_q_heads;
+  d.num_kv_heads = b->num_kv_heads;
+  d.head_dim = b->head_dim;
+  d.block_size = b->block_size;
+  d.bps = p.bps;
+  d.nsplit_max = p.nsplit;
+  d.nsplit_tail = p.nsplit;
+  d.skip_blocks = nullptr;
+  d.slot_base = 0;
+  d.shared_split_keys = 1;
+  d.stream = st;
+  return device_status(pa::launch_decode_merge(d), "pa_mixed_step merge launch");
+}
+
 pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* seq_lens,
                            const int32_t* query_start_loc, int32_t num_chunks, int32_t total_q,

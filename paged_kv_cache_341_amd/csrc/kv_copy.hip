@@ -19,7 +19,9 @@ constexpr int kCopyThreads = 256;
 __global__ __launch_bounds__(kCopyThreads) void kv_append_kernel(
     char* __restrict__ k_cache, char* __restrict__ v_cache, const char* __restrict__ k_new,
     const char* __restrict__ v_new, const int64_t* __restrict__ slot_mapping,
-    int64_t total_chunks, int chunks_per_row, int num_kv_heads, int block_size) {
+    int64_t total_chunks, int chunks_per_row, int num_kv_heads, int block_size,
+    int* __restrict__ zero_words, int num_zero_words) {
+  if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < num_zero_words) zero_words[threadIdx.x] = 0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x;
        i < total_chunks; i += stride) {
@@ -68,11 +70,12 @@ static unsigned grid_for(int64_t total) {
 hipError_t launch_append(const AppendArgs& a) {
   const int chunks_per_row = a.head_dim * a.elem_bytes / 16;
   const int64_t total = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * chunks_per_row;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_append_kernel, dim3(grid_for(total)), dim3(kCopyThreads), 0, a.stream,
-                     static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
+  if (total == 0 && a.num_zero_words == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(std::max(1u, grid_for(total))), dim3(kCopyThreads), 0,
+                     a.stream, static_cast<char*>(a.k_cache), static_cast<char*>(a.v_cache),
                      static_cast<const char*>(a.k_new), static_cast<const char*>(a.v_new),
-                     a.slot_mapping, total, chunks_per_row, a.num_kv_heads, a.block_size);
+                     a.slot_mapping, total, chunks_per_row, a.num_kv_heads, a.block_size,
+                     a.zero_words, a.num_zero_words);
   return hipGetLastError();
 }
 

@@ -50,6 +50,34 @@ struct AppendArgs {
   const void* v_new;
   const int64_t* slot_mapping;
   int num_tokens, num_kv_heads, head_dim, block_size, elem_bytes;
+  int* zero_words;               // optional: words set to 0 by the append launch (counters of a
+  int num_zero_words;            // kernel that runs next on the same stream), at most 64
+  hipStream_t stream;
+};
+
+// One launch of prefill chunks and decode splits together (bf16, D 128, B 16), after the append.
+struct MixedArgs {
+  // chunks
+  void* chunk_out;
+  const void* chunk_q;
+  const int32_t* chunk_tables;
+  const int32_t* chunk_seq_lens;
+  const int32_t* query_start_loc;
+  int num_chunks, chunk_max_blocks_per_seq;
+  // decodes
+  void* dec_out;
+  const void* dec_q;
+  const int32_t* dec_tables;
+  const int32_t* dec_seq_lens;
+  int num_seqs, dec_max_blocks_per_seq, bps, nsplit_max;
+  float* ws_ml;
+  float* ws_acc;
+  int* queues;                   // two work counters, zero when the kernel starts
+  // shared
+  const void* k_cache;
+  const void* v_cache;
+  int num_q_heads, num_kv_heads, num_workgroups;
+  float scale_log2;
   hipStream_t stream;
 };
 
@@ -86,6 +114,9 @@ struct SharedPrefixArgs {
 
 hipError_t launch_shared_prefix(const SharedPrefixArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_mixed(const MixedArgs& a);
+// the decode merge alone (after launch_mixed wrote the split partials)
+hipError_t launch_decode_merge(const DecodeArgs& a);
 hipError_t launch_append(const AppendArgs& a);
 hipError_t launch_cow(const CowArgs& a);
 hipError_t launch_hbm_probe(const void* src, size_t bytes, uint32_t* sink, int num_workgroups,

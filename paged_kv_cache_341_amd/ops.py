@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED
                 3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_DEVICE"}
 
 EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_grouped",
-            "pa_decode_grouped_workspace_size", "pa_prefill_chunk",
+            "pa_decode_grouped_workspace_size", "pa_mixed_step", "pa_mixed_workspace_size",
+            "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
             "pa_last_error", "pa_hbm_read_probe", "swap_blocks")
 # the native block manager (include/block_manager.h), bound in native_block_manager.py
@@ -44,6 +45,26 @@ class PagedAttnError(RuntimeError):
 _lib = None
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+
+class MixedBatch(ctypes.Structure):
+    """pa_mixed_batch (pagedattn.h), field for field."""
+    _fields_ = [
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p),
+        ("num_new_tokens", ctypes.c_int32),
+        ("chunk_out", ctypes.c_void_p), ("chunk_q", ctypes.c_void_p),
+        ("chunk_tables", ctypes.c_void_p), ("chunk_seq_lens", ctypes.c_void_p),
+        ("query_start_loc", ctypes.c_void_p), ("num_chunks", ctypes.c_int32),
+        ("chunk_total_q", ctypes.c_int32), ("chunk_max_q_len", ctypes.c_int32),
+        ("chunk_max_seq_len", ctypes.c_int32), ("chunk_max_blocks_per_seq", ctypes.c_int32),
+        ("dec_out", ctypes.c_void_p), ("dec_q", ctypes.c_void_p), ("dec_tables", ctypes.c_void_p),
+        ("dec_seq_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32),
+        ("dec_max_seq_len", ctypes.c_int32), ("dec_max_blocks_per_seq", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+    ]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -78,6 +99,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     _vp]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_mixed_step.restype = ctypes.c_int
+    lib.pa_mixed_step.argtypes = [ctypes.POINTER(MixedBatch), _vp, _sz, _vp]
+    lib.pa_mixed_workspace_size.restype = _sz
+    lib.pa_mixed_workspace_size.argtypes = [_i32] * 6
     lib.swap_blocks.restype = ctypes.c_int
     lib.swap_blocks.argtypes = [_vp] * 5 + [_i32] * 6 + [ctypes.c_int, _vp]
     lib.pa_hbm_read_probe.restype = ctypes.c_int
@@ -190,6 +215,66 @@ def pa_decode_grouped(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                                ws_bytes, _stream(q, stream))
     _check(st)
     return out
+
+
+def pa_mixed_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            block_size: int, dec_max_seq_len: int) -> int:
+    return int(load_library().pa_mixed_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                       head_dim, block_size, dec_max_seq_len))
+
+
+def pa_mixed_step(k_cache: torch.Tensor, v_cache: torch.Tensor, scale: float, *,
+                  k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                  slot_mapping: Optional[torch.Tensor] = None,
+                  chunk_out: Optional[torch.Tensor] = None, chunk_q: Optional[torch.Tensor] = None,
+                  chunk_tables: Optional[torch.Tensor] = None,
+                  chunk_seq_lens: Optional[torch.Tensor] = None,
+                  query_start_loc: Optional[torch.Tensor] = None, chunk_max_q_len: int = 0,
+                  chunk_max_seq_len: int = 0, dec_out: Optional[torch.Tensor] = None,
+                  dec_q: Optional[torch.Tensor] = None, dec_tables: Optional[torch.Tensor] = None,
+                  dec_seq_lens: Optional[torch.Tensor] = None, dec_max_seq_len: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append, chunk attention and decode attention of one iteration (see pagedattn.h)."""
+    lib = load_library()
+    _contig(k_cache, v_cache)
+    NB, Hkv, B, D = k_cache.shape
+    b = MixedBatch()
+    b.k_cache, b.v_cache = _ptr(k_cache), _ptr(v_cache)
+    b.num_kv_heads, b.head_dim, b.block_size, b.num_blocks = Hkv, D, B, NB
+    b.scale, b.dtype = float(scale), _dtype_code(k_cache)
+    Hq = None
+    if slot_mapping is not None and slot_mapping.numel() > 0:
+        _contig(k_new, v_new, slot_mapping)
+        _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+        b.k_new, b.v_new, b.slot_mapping = _ptr(k_new), _ptr(v_new), _ptr(slot_mapping)
+        b.num_new_tokens = slot_mapping.numel()
+    if chunk_q is not None and chunk_q.shape[0] > 0:
+        _contig(chunk_out, chunk_q, chunk_tables, chunk_seq_lens, query_start_loc)
+        _need(all(t.dtype == torch.int32 for t in (chunk_tables, chunk_seq_lens,
+                                                    query_start_loc)), "chunk indices must be int32")
+        Hq = chunk_q.shape[1]
+        b.chunk_out, b.chunk_q = _ptr(chunk_out), _ptr(chunk_q)
+        b.chunk_tables, b.chunk_seq_lens = _ptr(chunk_tables), _ptr(chunk_seq_lens)
+        b.query_start_loc = _ptr(query_start_loc)
+        b.num_chunks, b.chunk_total_q = chunk_seq_lens.numel(), chunk_q.shape[0]
+        b.chunk_max_q_len, b.chunk_max_seq_len = int(chunk_max_q_len), int(chunk_max_seq_len)
+        b.chunk_max_blocks_per_seq = chunk_tables.shape[1]
+    if dec_q is not None and dec_q.shape[0] > 0:
+        _contig(dec_out, dec_q, dec_tables, dec_seq_lens)
+        _need(dec_tables.dtype == torch.int32 and dec_seq_lens.dtype == torch.int32,
+              "decode indices must be int32")
+        _need(Hq is None or Hq == dec_q.shape[1], "chunk and decode head counts differ")
+        Hq = dec_q.shape[1]
+        b.dec_out, b.dec_q = _ptr(dec_out), _ptr(dec_q)
+        b.dec_tables, b.dec_seq_lens = _ptr(dec_tables), _ptr(dec_seq_lens)
+        b.num_seqs, b.dec_max_seq_len = dec_seq_lens.numel(), int(dec_max_seq_len)
+        b.dec_max_blocks_per_seq = dec_tables.shape[1]
+    b.num_q_heads = Hkv if Hq is None else Hq
+    need = pa_mixed_workspace_size(b.num_seqs, b.num_q_heads, Hkv, D, B, b.dec_max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k_cache.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.pa_mixed_step(ctypes.byref(b), _ptr(workspace), ws_bytes, _stream(k_cache, stream)))
 
 
 def pa_prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,

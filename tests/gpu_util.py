@@ -84,6 +84,37 @@ def run_decode_grouped(batch, group_start, shared_blocks, max_group_size, max_se
     return out
 
 
+def run_mixed_step(m, device="cuda", workspace=None):
+    """pa_mixed_step on a workloads.MixedStep: append, chunks and decodes in one call.  Returns
+    (chunk_out, dec_out)."""
+    nb = m.k_cache.shape[0]
+    checks.check_slots(m.slot_mapping, nb, m.block_size)
+    C = m.chunk_seq_lens.shape[0]
+    chunk_out = dec_out = None
+    kw = {}
+    if C:
+        mq = int(np.diff(m.query_start_loc).max())
+        msl = int(m.chunk_seq_lens.max())
+        checks.check_tables(m.chunk_tables, m.chunk_seq_lens, nb, m.block_size, msl)
+        checks.check_chunks(m.query_start_loc, m.chunk_seq_lens, m.q_chunk.shape[0], mq)
+        chunk_out = torch.empty_like(m.q_chunk)
+        kw.update(chunk_out=chunk_out, chunk_q=m.q_chunk,
+                  chunk_tables=dev_i32(m.chunk_tables, device),
+                  chunk_seq_lens=dev_i32(m.chunk_seq_lens, device),
+                  query_start_loc=dev_i32(m.query_start_loc, device), chunk_max_q_len=mq,
+                  chunk_max_seq_len=msl)
+    S = m.decode_seq_lens.shape[0]
+    if S:
+        dmsl = int(m.decode_seq_lens.max())
+        checks.check_tables(m.decode_tables, m.decode_seq_lens, nb, m.block_size, dmsl)
+        dec_out = torch.empty_like(m.q_decode)
+        kw.update(dec_out=dec_out, dec_q=m.q_decode, dec_tables=dev_i32(m.decode_tables, device),
+                  dec_seq_lens=dev_i32(m.decode_seq_lens, device), dec_max_seq_len=dmsl)
+    ops.pa_mixed_step(m.k_cache, m.v_cache, m.scale, k_new=m.k_new, v_new=m.v_new,
+                      slot_mapping=dev_i64(m.slot_mapping, device), workspace=workspace, **kw)
+    return chunk_out, dec_out
+
+
 def run_prefill(q, k_cache, v_cache, tables, seq_lens, qsl, scale, device="cuda"):
     total_q = q.shape[0]
     max_q = int(np.diff(qsl).max())

@@ -101,6 +101,56 @@ def test_grouped_workspace_size():
     assert ops.pa_decode_grouped_workspace_size(4, 6, 4, 128, 16, 100) == 0
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=30), INV), (dict(scale=0.0), INV), (dict(dec_q=None), INV),
+    (dict(dec_max_seq_len=200), INV), (dict(num_new_tokens=3), INV),
+    (dict(num_chunks=2, chunk_total_q=10, chunk_max_q_len=20, chunk_max_seq_len=30,
+          chunk_max_blocks_per_seq=4, chunk_out=P, chunk_q=P, chunk_tables=P,
+          chunk_seq_lens=P, query_start_loc=P), INV),
+    (dict(dtype=0), UNS), (dict(head_dim=64), UNS), (dict(num_q_heads=128), UNS),
+    (dict(num_seqs=3000), UNS), (dict(_wsb=16), WS),
+])
+def test_mixed_step_rejects(kw, status):
+    kw = dict(kw)
+    wsb = kw.pop("_wsb", 1 << 30)
+    b = ops.MixedBatch()
+    b.k_cache = b.v_cache = P
+    b.num_q_heads, b.num_kv_heads, b.head_dim, b.block_size, b.num_blocks = 32, 8, 128, 16, 100
+    b.scale, b.dtype = 0.1, 1
+    b.num_seqs, b.dec_max_seq_len, b.dec_max_blocks_per_seq = 4, 100, 8
+    b.dec_out = b.dec_q = b.dec_tables = b.dec_seq_lens = P
+    for k, v in kw.items():
+        setattr(b, k, v)
+    lib = ops.load_library()
+    assert lib.pa_mixed_step(None, P, wsb, None) == INV
+    assert lib.pa_mixed_step(ctypes.byref(b), P, wsb, None) == status
+    assert lib.pa_last_error().decode().startswith("pa_mixed_step")
+
+
+def test_mixed_batch_layout(tmp_path):
+    """The ctypes mirror of pa_mixed_batch has the C layout: every field's offset and the size,
+    as gcc lays the header's struct out."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    names = [f[0] for f in ops.MixedBatch._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"pagedattn.h\"\n"
+                   "int main(void) {\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(pa_mixed_batch, {n}));\n' for n in names)
+                   + '  printf("%zu\\n", sizeof(pa_mixed_batch));\n  return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o",
+                    str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    want = [getattr(ops.MixedBatch, n).offset for n in names] + [ctypes.sizeof(ops.MixedBatch)]
+    assert got == want
+    assert ops.pa_mixed_workspace_size(0, 32, 8, 128, 16, 0) == 256
+    assert ops.pa_mixed_workspace_size(192, 32, 8, 128, 16, 16384) > 192 * 32 * 130 * 4
+
+
 def _prefill(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, sl=P, qsl=P, C=8, T=4096, maxq=512, maxlen=8704,
              Hq=32, Hkv=8, D=128, B=16, NB=1000, MB=600, scale=0.1, dtype=1)

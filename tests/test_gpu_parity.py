@@ -14,8 +14,8 @@ from paged_kv_cache_341_amd import checks, ops
 from paged_kv_cache_341_amd.block_manager import shared_prefix_groups
 from tests.gpu_util import (ATOL, F32_ATOL, F32_RTOL, RTOL, assert_close, compact, dev_i32,
                             dev_i64, raw,
-                            run_append, run_cow, run_decode, run_decode_grouped, run_prefill, say,
-                            widen)
+                            run_append, run_cow, run_decode, run_decode_grouped, run_mixed_step,
+                            run_prefill, say, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -433,3 +433,56 @@ def test_swap_out_and_in_through_pinned_host_pool():
         wk, wv = ref.swap_ref(gk, gv, raw(hk), raw(hv), p)
         assert np.array_equal(raw(k), wk) and np.array_equal(raw(v), wv)
     assert torch.equal(decode(), before)
+
+
+# ------------------------------------------------------------------------------ single launch
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_mixed_step_single_launch_ragged(G):
+    """pa_mixed_step on a small ragged iteration: 5 chunks of {1, 37, 256, 300, 513} rows over
+    prefixes {0, 5, 4000, 16, 1500} and 40 lognormal decodes.  The pool after the call is the
+    oracle's append, bit for bit; every chunk and decode row matches the oracle; chunk rows
+    are bit-identical to pa_prefill_chunk on the same pool (the same per-item code)."""
+    say(f"case: mixed step single launch, ragged, G={G}")
+    m = W.mixed_bf16(device=DEV, seed=2000 + G, num_chunks=5, chunk_lens=[1, 37, 256, 300, 513],
+                     prefixes=[0, 5, 4000, 16, 1500], num_decode=40, cap=6000,
+                     num_q_heads=2 * G, num_kv_heads=2)
+    bk, bv = raw(m.k_cache), raw(m.v_cache)
+    cout, dout = run_mixed_step(m)
+    wk, wv = ref.append_ref(bk, bv, raw(m.k_new), raw(m.v_new), m.slot_mapping)
+    kc, vc = raw(m.k_cache), raw(m.v_cache)
+    assert np.array_equal(kc, wk) and np.array_equal(vc, wv)
+    want = ref.prefill_ref(raw(m.q_chunk), kc, vc, m.chunk_tables, m.chunk_seq_lens,
+                           m.query_start_loc, m.scale, "bf16")
+    assert_close(widen(cout), want, ATOL, RTOL, "mixed chunks")
+    alone = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
+                        m.query_start_loc, m.scale)
+    assert torch.equal(cout, alone)
+    want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, "mixed decodes")
+
+
+def test_mixed_step_single_launch_full_size():
+    """The full mixed iteration (8 x 512-row chunks, 192 decodes) in one pa_mixed_step call,
+    twice with the same garbage-filled workspace (the counters are reset by the call): pool
+    bit-exact, chunk rows bit-identical to pa_prefill_chunk, decodes sampled against the
+    oracle, and the second call's outputs equal the first's."""
+    say("case: mixed_bf16 full size, single launch")
+    m = W.mixed_bf16(device=DEV)
+    bk, bv = raw(m.k_cache), raw(m.v_cache)
+    n = ops.pa_mixed_workspace_size(192, 32, 8, 128, 16, int(m.decode_seq_lens.max()))
+    ws = torch.full((n,), 0x7F, dtype=torch.uint8, device=DEV)
+    cout, dout = run_mixed_step(m, workspace=ws)
+    wk, wv = ref.append_ref(bk, bv, raw(m.k_new), raw(m.v_new), m.slot_mapping)
+    kc, vc = raw(m.k_cache), raw(m.v_cache)
+    assert np.array_equal(kc, wk) and np.array_equal(vc, wv)
+    del wk, wv, bk, bv
+    alone = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
+                        m.query_start_loc, m.scale)
+    assert torch.equal(cout, alone)
+    seqs = list(range(0, 192, 7)) + [int(np.argmax(m.decode_seq_lens))]
+    want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
+                          "bf16", seqs=seqs)
+    assert_close(widen(dout)[seqs], want[seqs], ATOL, RTOL, "mixed single-launch decodes")
+    cout2, dout2 = run_mixed_step(m, workspace=ws)     # appends the same bytes again
+    assert torch.equal(cout2, cout) and torch.equal(dout2, dout)
