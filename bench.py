@@ -39,10 +39,12 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 # HBM bytes per launch of pa_decode_split_kernel on decode_bf16, from two rocprofv3 passes
 # (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a plain 1 GiB copy; the summary is in
 # profiles/pa_decode.all_decode_workloads.md).  They describe the kernel source with this
-# SHA-256 prefix only; after any change to it the figure is reported as null.
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_341_amd", "csrc", "pa_decode.hip")
-MEASURED_TRAFFIC = {"sha256_prefix": "268e23e461f9ae16", "fetch_kib": 243671.9,
-                    "write_kib": 4309.1, "fetch_scale": 2.0, "write_scale": 1.0}
+# SHA-256 prefix only (pa_decode.hip and decode_item.hpp together); after any change to them
+# the figure is reported as null.
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_341_amd", "csrc", f)
+               for f in ("pa_decode.hip", "decode_item.hpp")]
+MEASURED_TRAFFIC = {"sha256_prefix": "d5da7e284e5df8d9", "fetch_kib": 243669.7,
+                    "write_kib": 4309.3, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def log(msg: str) -> None:
@@ -104,8 +106,11 @@ def copy_calibration(mib: int, steps: int = 10) -> None:
 
 def measured_traffic():
     """HBM bytes per decode_bf16 split launch from the counters, or None if the kernel changed."""
-    with open(DECODE_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in DECODE_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
     m = MEASURED_TRAFFIC
     if sha != m["sha256_prefix"]:
         return None
