@@ -216,6 +216,12 @@ __device__ __forceinline__ void prefill_item(
     load_tile(kt + 3, kload, vload);
 
     if (kt * kKvTile < kv_end_w) {
+      // scores of the next tile first: they depend only on staged K and the resident Q, so the
+      // matrix cores work through them while the softmax of tile kt below runs on the vector
+      // ALUs (a wave that needs no key of tile kt needs none of tile kt+1 either, and past the
+      // last tile the result is simply never used)
+      qk(knext, nxt);
+
       // --------------------------------------------------------------- online softmax (max)
       const bool need_mask = kt * kKvTile + kKvTile - 1 > prefix + t_lo_w;
       if (need_mask) {
@@ -244,11 +250,6 @@ __device__ __forceinline__ void prefill_item(
 #pragma unroll
           for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
       }
-
-      // scores of the next tile (independent of what follows, so the matrix cores run while
-      // the exponentials below are computed); a wave that needs no key of tile kt needs none of
-      // tile kt+1 either, and past the last tile the result is simply never used
-      qk(knext, nxt);
 
       // --------------------------------------------------------------- probabilities
       const float mc = m_run * scale_log2;
