@@ -268,6 +268,17 @@ def bench_mixed(steps, warmup, overlap=False):
 
     t_step = time_calls(step, steps, warmup)
     t_single = time_calls(single, steps, warmup)
+    # the same three-launch iteration captured once in a HIP graph and replayed
+    side_cap = torch.cuda.Stream()
+    side_cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side_cap):
+        step()
+    torch.cuda.current_stream().wait_stream(side_cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    t_graph = time_calls(graph.replay, steps, warmup)
     t_over = time_calls(step_overlapped, steps, warmup) if overlap else None
     t_app = time_calls(append, steps, warmup)
     t_pre = time_calls(prefill, steps, warmup)
@@ -285,7 +296,8 @@ def bench_mixed(steps, warmup, overlap=False):
         prefill_mfma_frac=tflops / BF16_PEAK_TFLOPS,
         decode_ms=t_dec[0], decode_kv_bytes=dec_bytes,
         decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9,
-        single_launch_ms=t_single[0], single_launch_tokens_per_s=T / (t_single[0] * 1e-3))
+        single_launch_ms=t_single[0], single_launch_tokens_per_s=T / (t_single[0] * 1e-3),
+        graph_replay_ms=t_graph[0], graph_replay_tokens_per_s=T / (t_graph[0] * 1e-3))
     if t_over is not None:
         res.update(overlapped_tokens_per_s=T / (t_over[0] * 1e-3), overlapped_ms_per_step=t_over[0])
         log(f"mixed step, chunks and decodes on two streams: {t_over[0] * 1e3:.1f} us -> "
@@ -296,6 +308,8 @@ def bench_mixed(steps, warmup, overlap=False):
         f"{res['decode_gbps']:.0f} GB/s")
     log(f"mixed step as one pa_mixed_step call (single launch): {t_single[0] * 1e3:.1f} us -> "
         f"{res['single_launch_tokens_per_s']:.0f} tok/s")
+    log(f"mixed step replayed from a HIP graph: {t_graph[0] * 1e3:.1f} us -> "
+        f"{res['graph_replay_tokens_per_s']:.0f} tok/s")
     return res
 
 

@@ -486,3 +486,93 @@ def test_mixed_step_single_launch_full_size():
     assert_close(widen(dout)[seqs], want[seqs], ATOL, RTOL, "mixed single-launch decodes")
     cout2, dout2 = run_mixed_step(m, workspace=ws)     # appends the same bytes again
     assert torch.equal(cout2, cout) and torch.equal(dout2, dout)
+
+
+# ------------------------------------------------------------------------------ graph capture
+def _replays_match(step, outs, replays=3):
+    """Eager run, capture, then replays with eager work between them: every replay must give
+    the eager outputs bit for bit."""
+    step()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(replays):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            assert torch.equal(o, w)
+        step()                                  # eager work between replays
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            assert torch.equal(o, w)
+
+
+def test_graph_capture_of_an_iteration():
+    """kv_append, pa_prefill_chunk and pa_decode (split and merge) captured in one HIP graph,
+    then the same iteration as one pa_mixed_step call captured in another: the calls allocate
+    nothing, synchronise nothing and record no memset, so replays match eager runs."""
+    say("case: graph capture of append + chunks + decodes, and of pa_mixed_step")
+    m = W.mixed_bf16(device=DEV, seed=2100, num_chunks=3, chunk_lens=[64, 200, 7],
+                     prefixes=[100, 3000, 0], num_decode=24, cap=5000)
+    nb = m.k_cache.shape[0]
+    checks.check_slots(m.slot_mapping, nb, 16)
+    mq, msl = int(np.diff(m.query_start_loc).max()), int(m.chunk_seq_lens.max())
+    dmsl = int(m.decode_seq_lens.max())
+    checks.check_tables(m.chunk_tables, m.chunk_seq_lens, nb, 16, msl)
+    checks.check_tables(m.decode_tables, m.decode_seq_lens, nb, 16, dmsl)
+    sm = dev_i64(m.slot_mapping)
+    ct, cl, qsl = dev_i32(m.chunk_tables), dev_i32(m.chunk_seq_lens), dev_i32(m.query_start_loc)
+    dt, dl = dev_i32(m.decode_tables), dev_i32(m.decode_seq_lens)
+    cout, dout = torch.empty_like(m.q_chunk), torch.empty_like(m.q_decode)
+    dws = torch.empty(max(ops.pa_decode_workspace_size(24, 32, 8, 128, 16, dmsl), 16),
+                      dtype=torch.uint8, device=DEV)
+
+    def step():
+        ops.kv_append(m.k_cache, m.v_cache, m.k_new, m.v_new, sm)
+        ops.pa_prefill_chunk(cout, m.q_chunk, m.k_cache, m.v_cache, ct, cl, qsl, mq, msl, m.scale)
+        ops.pa_decode(dout, m.q_decode, m.k_cache, m.v_cache, dt, dl, dmsl, m.scale,
+                      workspace=dws)
+
+    _replays_match(step, [cout, dout])
+    mws = torch.empty(ops.pa_mixed_workspace_size(24, 32, 8, 128, 16, dmsl), dtype=torch.uint8,
+                      device=DEV)
+    cout2, dout2 = torch.empty_like(cout), torch.empty_like(dout)
+
+    def single():
+        ops.pa_mixed_step(m.k_cache, m.v_cache, m.scale, k_new=m.k_new, v_new=m.v_new,
+                          slot_mapping=sm, chunk_out=cout2, chunk_q=m.q_chunk, chunk_tables=ct,
+                          chunk_seq_lens=cl, query_start_loc=qsl, chunk_max_q_len=mq,
+                          chunk_max_seq_len=msl, dec_out=dout2, dec_q=m.q_decode,
+                          dec_tables=dt, dec_seq_lens=dl, dec_max_seq_len=dmsl, workspace=mws)
+
+    _replays_match(single, [cout2, dout2])
+    assert torch.equal(cout2, cout)
+
+
+def test_graph_capture_of_grouped_decode():
+    say("case: graph capture of pa_decode_grouped")
+    b = W.make_grouped_decode(GROUPS, 8, 2, 128, seed=2200, device=DEV)
+    msl = b.max_seq_len
+    bt, sl = dev_i32(b.block_tables), dev_i32(b.seq_lens)
+    gs, sb = dev_i32(b.extra["group_start"]), dev_i32(b.extra["shared_blocks"])
+    out = torch.empty_like(b.q)
+    ws = torch.empty(ops.pa_decode_grouped_workspace_size(b.num_seqs, 8, 2, 128, 16, msl),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        ops.pa_decode_grouped(out, b.q, b.k_cache, b.v_cache, bt, sl, gs, sb,
+                              b.extra["max_group_size"], msl, b.scale, workspace=ws)
+
+    _replays_match(step, [out])
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, "grouped decode replayed")
