@@ -76,6 +76,37 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   const float* ml = ws_ml + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * 2;
   const float* acc = ws_acc + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * D;
 
+  constexpr int kFast = 8;
+  if (nsplit <= kFast) {
+    // Up to kFast splits: the statistics and every partial are requested together, one round
+    // trip, and summed in split order as below.
+    float a[kFast][kPer];
+#pragma unroll
+    for (int u = 0; u < kFast; ++u)
+      if (u < nsplit)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a[u][e] = acc[static_cast<size_t>(u) * D + lane + e * kWave];
+    const float mi = lane < nsplit ? ml[2 * lane] : kNegInf;
+    const float li = lane < nsplit ? ml[2 * lane + 1] : 0.f;
+    const float Mf = group_max<kWave>(mi);
+    const float w = lane < nsplit ? exp2f(mi - Mf) : 0.f;
+    const float inv = 1.f / group_sum<kWave>(w * li);
+    float num[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFast; ++u)
+      if (u < nsplit) {
+        const float wu = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), u));
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) num[e] = fmaf(wu, a[u][e], num[e]);
+      }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      store_out(out + static_cast<size_t>(row) * D + lane + e * kWave, num[e] * inv);
+    return;
+  }
+
   float M = kNegInf;
   for (int i = lane; i < nsplit; i += kWave) M = fmaxf(M, ml[2 * i]);
   M = group_max<kWave>(M);
