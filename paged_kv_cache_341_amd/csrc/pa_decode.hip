@@ -40,6 +40,10 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   // order; with this order each XCD gets an even share of every split index (instead of one
   // XCD holding every sequence's first split), and the beams that share a block read it
   // through the same XCD's L2.
+  // Workgroups are dispatched in launch order, and on a CU the oldest waves win instruction
+  // issue, so the splits dispatched last would be starved by older workgroups and end the
+  // kernel late; the second half of the split range runs at raised wave priority instead.
+  if (blockIdx.y * 2 >= gridDim.y) __builtin_amdgcn_s_setprio(3);
   decode_split_item<T, D, G, B, kDecodeWaves>(
       out, ws_ml, ws_acc, q, k_cache, v_cache, block_tables, seq_lens, skip_blocks, slot_base,
       num_kv_heads, max_blocks_per_seq, bps, nsplit_max, scale_log2,
@@ -60,10 +64,51 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
     int slot_base, int shared_split_keys, int num_rows, int num_q_heads, int bps,
     int nsplit_max) {
   constexpr int kPer = D / kWave;
+  constexpr int kFast = 8;
   const int row = blockIdx.x * kMergeWaves + static_cast<int>(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   if (row >= num_rows) return;
   const int s = row / num_q_heads;
+
+  if (skip_blocks == nullptr && slot_base == 0 && nsplit_max <= kFast) {
+    // Plain decode with at most kFast split slots per row: every slot of the row exists in the
+    // workspace, so its statistics and partials are requested together with the sequence
+    // length (one round trip instead of two); slots past the row's split count are dropped by
+    // selection, never used.
+    const float* ml = ws_ml + static_cast<size_t>(row) * nsplit_max * 2;
+    const float* acc = ws_acc + static_cast<size_t>(row) * nsplit_max * D;
+    float a[kFast][kPer];
+#pragma unroll
+    for (int u = 0; u < kFast; ++u)
+      if (u < nsplit_max)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a[u][e] = acc[static_cast<size_t>(u) * D + lane + e * kWave];
+    const float mraw = lane < nsplit_max ? ml[2 * lane] : 0.f;
+    const float lraw = lane < nsplit_max ? ml[2 * lane + 1] : 0.f;
+    const int L = seq_lens[s];
+    const int nsplit = ((L + B - 1) / B + bps - 1) / bps;
+    if (nsplit <= 1) return;                      // written directly by the split kernel
+    const float mi = lane < nsplit ? mraw : kNegInf;
+    const float li = lane < nsplit ? lraw : 0.f;
+    const float Mf = group_max<kWave>(mi);
+    const float w = lane < nsplit ? exp2f(mi - Mf) : 0.f;
+    const float inv = 1.f / group_sum<kWave>(w * li);
+    float num[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFast; ++u)
+      if (u < nsplit) {
+        const float wu = u32_as_f32(__builtin_amdgcn_readlane(f32_as_u32(w), u));
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) num[e] = fmaf(wu, a[u][e], num[e]);
+      }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      store_out(out + static_cast<size_t>(row) * D + lane + e * kWave, num[e] * inv);
+    return;
+  }
+
   const int L = seq_lens[s];
   const int nblk = (L + B - 1) / B;
   // partials of this row: the shared-prefix splits end at slot_base, the splits of the rest
@@ -76,7 +121,6 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   const float* ml = ws_ml + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * 2;
   const float* acc = ws_acc + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * D;
 
-  constexpr int kFast = 8;
   if (nsplit <= kFast) {
     // Up to kFast splits: the statistics and every partial are requested together, one round
     // trip, and summed in split order as below.
