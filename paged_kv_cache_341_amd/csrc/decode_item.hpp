@@ -68,14 +68,16 @@ __device__ __forceinline__ void store_out(bf16_t* p, float v) {
 // max(bps * B * G, Waves * G * D) floats (scores, then the waves' partial outputs), `red`
 // Waves x G floats, `stat_m` and `stat_l` G floats each.
 // `Batch` blocks per wave are loaded together before their math (0: 64 tokens' worth).
-template <typename T, int D, int G, int B, int Waves, int Batch = 0>
+// With `Prio`, the K phase runs at wave priority 2 and the V phase at 0, each one band higher
+// when `late` (a split dispatched late): splits that have made less progress issue first.
+template <typename T, int D, int G, int B, int Waves, int Batch = 0, bool Prio = false>
 __device__ __forceinline__ void decode_split_item(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ skip_blocks, int slot_base, int num_kv_heads,
     int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2, int s, int kvh,
-    int split, float* smem, float (*red)[G], float* stat_m, float* stat_l) {
+    int split, float* smem, float (*red)[G], float* stat_m, float* stat_l, bool late = false) {
   using S = DecodeShape<T, D, G, B>;
   constexpr int kBlock = B;
   constexpr int kDecodeBatch = Batch > 0 ? Batch : S::kBatch;
@@ -100,6 +102,11 @@ __device__ __forceinline__ void decode_split_item(
   const int Hq = num_kv_heads * G;
   const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks_per_seq;
   const size_t slab = static_cast<size_t>(kBlock) * D;   // elements per (block, kv head)
+
+  if constexpr (Prio) {
+    if (late) __builtin_amdgcn_s_setprio(3);
+    else __builtin_amdgcn_s_setprio(2);
+  }
 
   // ---------------------------------------------------------------- phase 1: scores
   {
@@ -186,6 +193,10 @@ __device__ __forceinline__ void decode_split_item(
   __syncthreads();
 
   // ------------------------------------------------------------------ phase 3: p * V
+  if constexpr (Prio) {
+    if (late) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
   const int grp = lane / S::kW3;
   const int sub = lane % S::kW3;
   float acc[G][S::kAcc];

@@ -14,6 +14,11 @@
 //   phase 2  exact softmax statistics of the split: max and sum of exp2 per query head;
 //   phase 3  each wave reads the V slabs of the same blocks and accumulates p * V in fp32,
 //            lanes split over the head dimension again; waves are summed through LDS.
+// Wave priorities: on a CU the oldest waves win instruction issue, so workgroups dispatched
+// late (onto slots freed by finished splits) were starved by older ones and ended the kernel
+// late.  Each split therefore runs its K phase at a higher wave priority than its V phase, so
+// the splits that have made the least progress issue first, and the splits dispatched last
+// (the second half of the split index range) sit one band above the rest.
 // A split with the whole sequence writes the normalised output; otherwise it writes
 // (max, sum, unnormalised acc) and a merge kernel combines the splits in split order
 // (log-sum-exp weighting), so results do not depend on scheduling.
@@ -40,15 +45,13 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   // order; with this order each XCD gets an even share of every split index (instead of one
   // XCD holding every sequence's first split), and the beams that share a block read it
   // through the same XCD's L2.
-  // Workgroups are dispatched in launch order, and on a CU the oldest waves win instruction
-  // issue, so the splits dispatched last would be starved by older workgroups and end the
-  // kernel late; the second half of the split range runs at raised wave priority instead.
-  if (blockIdx.y * 2 >= gridDim.y) __builtin_amdgcn_s_setprio(3);
-  decode_split_item<T, D, G, B, kDecodeWaves>(
+  // The splits dispatched last are the second half of the split-index range (grid.y): they
+  // take the higher of the two priority bands (see decode_split_item).
+  decode_split_item<T, D, G, B, kDecodeWaves, 0, true>(
       out, ws_ml, ws_acc, q, k_cache, v_cache, block_tables, seq_lens, skip_blocks, slot_base,
       num_kv_heads, max_blocks_per_seq, bps, nsplit_max, scale_log2,
       static_cast<int>(blockIdx.x) / num_kv_heads, static_cast<int>(blockIdx.x) % num_kv_heads,
-      static_cast<int>(blockIdx.y), smem, red, stat_m, stat_l);
+      static_cast<int>(blockIdx.y), smem, red, stat_m, stat_l, blockIdx.y * 2 >= gridDim.y);
 }
 
 // Combine the splits of one (sequence, query head) row; one wave per row.  Lanes first read
