@@ -28,17 +28,21 @@
  *
  * Ownership: the caller owns every buffer.  Device pointers must be device memory of the
  * current HIP device; `stream` is a hipStream_t (NULL = the default stream).  The library never
- * allocates or frees memory, keeps no pointer after returning, and holds no mutable global state,
- * so calls from several host threads are safe.  Every call only enqueues work on `stream`: no
- * host synchronisation, no device-to-host copy.
+ * allocates or frees memory, keeps no pointer after returning, and holds no mutable global state
+ * beyond the checked-mode switch below, so calls from several host threads are safe.  Every call
+ * only enqueues work on `stream`: no host synchronisation, no device-to-host copy (except in
+ * checked mode).
  *
  * Errors: host scalars and pointers are checked before anything is enqueued; a failed check
  * returns a non-zero status, enqueues nothing, and sets a per-thread message readable through
  * pa_last_error().  Device contents (table entries, lengths, slots) are preconditions, not
  * checked: table entries read must lie in [0, num_blocks), 1 <= seq_lens[i] <= max_seq_len,
  * non-negative slots must be distinct and below num_blocks*block_size, copy destinations must be
- * distinct and never a source.  Violating them is undefined behaviour.  No C++ exception
- * crosses this interface.
+ * distinct and never a source.  Violating them is undefined behaviour.  In checked mode
+ * (pa_set_checked_mode, or the environment variable PA_CHECKED=1) every call first copies its
+ * index arrays to the host on `stream`, synchronises that stream, and returns
+ * PA_ERR_INVALID_ARGUMENT, enqueuing nothing, on the first violated precondition.  No C++
+ * exception crosses this interface.
  */
 #ifndef PAGEDATTN_H_
 #define PAGEDATTN_H_
@@ -286,6 +290,20 @@ const char* pa_status_string(pa_status s);
 
 /* Per-thread description of the last failed call on this thread ("" if none). */
 const char* pa_last_error(void);
+
+/*
+ * Checked mode, for callers that cannot trust their index arrays (debugging, untrusted input):
+ * when on, pa_decode, pa_decode_grouped, pa_prefill_chunk, pa_mixed_step, kv_append,
+ * cow_copy_blocks and swap_blocks validate their device-content preconditions on host copies
+ * (table entries used, seq_lens in [1, max_seq_len], query_start_loc rising from 0 to total_q
+ * with chunks no longer than max_q_len or their sequence, slots in range and distinct, copy
+ * pairs in range with distinct destinations that are never a source, group plans as
+ * pa_decode_grouped requires) before enqueuing anything.  Each such call synchronises its
+ * stream once.  Process-wide; off unless PA_CHECKED is set to a value other than "0".
+ * pa_set_checked_mode returns the previous setting (0 or 1); pa_checked_mode the current one.
+ */
+int pa_set_checked_mode(int enable);
+int pa_checked_mode(void);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <string>
 
+#include "checked.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -86,6 +87,17 @@ pa_status device_status(hipError_t e, const char* what) {
   return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// In checked mode, run a host-side check of device contents; a violation fails the call with
+// PA_ERR_INVALID_ARGUMENT before anything is enqueued.
+#define PA_CHECK_CONTENTS(name, expr)                                                      \
+  do {                                                                                     \
+    if (pa::checked::enabled()) {                                                          \
+      const std::string msg_ = (expr);                                                     \
+      if (!msg_.empty())                                                                   \
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s (checked mode): %s", name, msg_.c_str()); \
+    }                                                                                      \
+  } while (0)
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +114,10 @@ const char* pa_status_string(pa_status s) {
 }
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_set_checked_mode(int enable) { return pa::checked::set_enabled(enable != 0) ? 1 : 0; }
+
+int pa_checked_mode(void) { return pa::checked::enabled() ? 1 : 0; }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len) {
@@ -159,6 +175,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   // grid: x = num_seqs * num_kv_heads workgroups of 256 lanes, y = splits
   if (nsplit > 65535 || static_cast<int64_t>(num_seqs) * num_kv_heads > (int64_t{1} << 24))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+
+  PA_CHECK_CONTENTS("pa_decode",
+                    pa::checked::tables(static_cast<hipStream_t>(stream), block_tables, seq_lens,
+                                        num_seqs, max_blocks_per_seq, num_blocks, block_size,
+                                        max_seq_len));
 
   pa::DecodeArgs a{};
   a.out = out;
@@ -286,6 +307,13 @@ pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const
   float* ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ml_bytes);
   const float scale_log2 = scale * 1.4426950408889634f;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  PA_CHECK_CONTENTS("pa_decode_grouped",
+                    pa::checked::tables(st, block_tables, seq_lens, num_seqs, max_blocks_per_seq,
+                                        num_blocks, block_size, max_seq_len));
+  PA_CHECK_CONTENTS("pa_decode_grouped",
+                    pa::checked::groups(st, group_start, shared_blocks, block_tables, seq_lens,
+                                        num_seqs, num_groups, max_group_size, max_blocks_per_seq,
+                                        block_size));
 
   pa::SharedPrefixArgs sp{};
   sp.ws_ml = ws_ml;
@@ -448,6 +476,23 @@ pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspa
     return fail(PA_ERR_DEVICE, "pa_mixed_step: cannot read the device's compute-unit count");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (b->num_new_tokens > 0)
+    PA_CHECK_CONTENTS("pa_mixed_step", pa::checked::slots(st, b->slot_mapping, b->num_new_tokens,
+                                                          b->num_blocks, b->block_size));
+  if (b->num_chunks > 0) {
+    PA_CHECK_CONTENTS("pa_mixed_step chunks",
+                      pa::checked::chunks(st, b->query_start_loc, b->chunk_seq_lens,
+                                          b->num_chunks, b->chunk_total_q, b->chunk_max_q_len));
+    PA_CHECK_CONTENTS("pa_mixed_step chunks",
+                      pa::checked::tables(st, b->chunk_tables, b->chunk_seq_lens, b->num_chunks,
+                                          b->chunk_max_blocks_per_seq, b->num_blocks,
+                                          b->block_size, b->chunk_max_seq_len));
+  }
+  if (b->num_seqs > 0)
+    PA_CHECK_CONTENTS("pa_mixed_step decodes",
+                      pa::checked::tables(st, b->dec_tables, b->dec_seq_lens, b->num_seqs,
+                                          b->dec_max_blocks_per_seq, b->num_blocks,
+                                          b->block_size, b->dec_max_seq_len));
   int* queues = static_cast<int*>(workspace);
   char* ws = static_cast<char*>(workspace) + kMixedHeader;
   float* ws_ml = reinterpret_cast<float*>(ws);
@@ -569,6 +614,13 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   const int64_t tiles_max = (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 127) / 128;
   if (static_cast<int64_t>(num_chunks) * tiles_max * num_kv_heads > (int64_t{1} << 24))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: grid too large");
+  PA_CHECK_CONTENTS("pa_prefill_chunk",
+                    pa::checked::chunks(static_cast<hipStream_t>(stream), query_start_loc,
+                                        seq_lens, num_chunks, total_q, max_q_len));
+  PA_CHECK_CONTENTS("pa_prefill_chunk",
+                    pa::checked::tables(static_cast<hipStream_t>(stream), block_tables, seq_lens,
+                                        num_chunks, max_blocks_per_seq, num_blocks, block_size,
+                                        max_seq_len));
   pa::PrefillArgs a{};
   a.out = out;
   a.q = q;
@@ -603,6 +655,9 @@ pa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void*
     return fail(PA_ERR_INVALID_ARGUMENT, "kv_append: buffers must be 16-byte aligned");
   if ((head_dim * elem_bytes(dtype)) % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "kv_append: head_dim rows must be a multiple of 16 bytes");
+  PA_CHECK_CONTENTS("kv_append", pa::checked::slots(static_cast<hipStream_t>(stream),
+                                                    slot_mapping, num_tokens, num_blocks,
+                                                    block_size));
   pa::AppendArgs a{};
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -634,6 +689,9 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
       static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   if (block_bytes % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "cow_copy_blocks: block bytes must be a multiple of 16");
+  PA_CHECK_CONTENTS("cow_copy_blocks",
+                    pa::checked::pairs(static_cast<hipStream_t>(stream), block_pairs, num_pairs,
+                                       num_blocks, num_blocks, true));
   pa::CowArgs a{};
   a.dst_k = k_cache;
   a.dst_v = v_cache;
@@ -666,6 +724,9 @@ pa_status swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* s
       static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   if (block_bytes % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "swap_blocks: block bytes must be a multiple of 16");
+  PA_CHECK_CONTENTS("swap_blocks",
+                    pa::checked::pairs(static_cast<hipStream_t>(stream), block_pairs, num_pairs,
+                                       num_src_blocks, num_dst_blocks, false));
   pa::CowArgs a{};
   a.dst_k = dst_k;
   a.dst_v = dst_v;

@@ -27,7 +27,8 @@ EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_grouped",
             "pa_decode_grouped_workspace_size", "pa_mixed_step", "pa_mixed_workspace_size",
             "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
-            "pa_last_error", "pa_hbm_read_probe", "swap_blocks")
+            "pa_last_error", "pa_hbm_read_probe", "swap_blocks", "pa_set_checked_mode",
+            "pa_checked_mode")
 # the native block manager (include/block_manager.h), bound in native_block_manager.py
 BM_EXPORTED = ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append",
                "pa_bm_fork", "pa_bm_free", "pa_bm_blocks_needed", "pa_bm_seq_info",
@@ -109,6 +110,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
+    lib.pa_set_checked_mode.restype = ctypes.c_int
+    lib.pa_set_checked_mode.argtypes = [ctypes.c_int]
+    lib.pa_checked_mode.restype = ctypes.c_int
+    lib.pa_checked_mode.argtypes = []
     _lib = lib
     return lib
 
@@ -364,6 +369,16 @@ def pa_hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, num_workgroups: int
     _need(sink.numel() * sink.element_size() >= num_workgroups * 256 * 4, "sink too small")
     _check(lib.pa_hbm_read_probe(_ptr(src), nbytes, _ptr(sink), int(num_workgroups),
                                  _stream(src, stream)))
+
+
+def set_checked_mode(enable: bool) -> bool:
+    """Turn the library's checked mode on or off (see pagedattn.h); returns the previous
+    setting."""
+    return bool(load_library().pa_set_checked_mode(1 if enable else 0))
+
+
+def checked_mode() -> bool:
+    return bool(load_library().pa_checked_mode())
 
 
 def status_string(status: int) -> str:

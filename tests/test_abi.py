@@ -190,3 +190,16 @@ def test_read_probe_validation():
     assert lib.pa_hbm_read_probe(P, 0, P, 4, None) == INV
     assert lib.pa_hbm_read_probe(P + 8, 1024, P, 4, None) == INV    # misaligned
     assert lib.pa_hbm_read_probe(P, 1024, P, 0, None) == INV
+
+
+def test_checked_mode_switch():
+    """The checked-mode switch is process-wide and reports its previous setting (no device call
+    is made: the switch alone touches no GPU)."""
+    prev = ops.set_checked_mode(True)
+    try:
+        assert ops.checked_mode() is True
+        assert ops.set_checked_mode(False) is True
+        assert ops.checked_mode() is False
+        assert ops.set_checked_mode(False) is False
+    finally:
+        ops.set_checked_mode(prev)
