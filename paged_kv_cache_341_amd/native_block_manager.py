@@ -34,35 +34,45 @@ class _Stats(ctypes.Structure):
 _LIB = None
 
 
+def _bind(lib):
+    sig = {
+        "pa_bm_create": (_vp, [_i32, _i32, _i32, _vp, _vp]),
+        "pa_bm_destroy": (None, [_vp]),
+        "pa_bm_add_sequence": (ctypes.c_int, [_vp, _i64, _i64, _vp]),
+        "pa_bm_append": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _P32]),
+        "pa_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+        "pa_bm_free": (ctypes.c_int, [_vp, _i64]),
+        "pa_bm_blocks_needed": (_i64, [_vp, _i64, _i64]),
+        "pa_bm_seq_info": (ctypes.c_int, [_vp, _i64, _P64, _P32, _P32, _P64, _P64]),
+        "pa_bm_table": (ctypes.c_int, [_vp, _i64, _vp, _i32]),
+        "pa_bm_block_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp]),
+        "pa_bm_refcount": (_i32, [_vp, _i32, _i32]),
+        "pa_bm_preempt_latest": (ctypes.c_int, [_vp, _i32, _i64, _P64, _vp, _i32, _P32]),
+        "pa_bm_swap_in_earliest": (ctypes.c_int, [_vp, _P64, _vp, _i32, _P32]),
+        "pa_bm_resume_recompute": (ctypes.c_int, [_vp, _i64]),
+        "pa_bm_request_members": (ctypes.c_int, [_vp, _i64, _vp, _i32, _P32]),
+        "pa_bm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(_Stats)]),
+        "pa_bm_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
 def _lib():
     global _LIB
     if _LIB is None:
-        lib = ops.load_library()
-        sig = {
-            "pa_bm_create": (_vp, [_i32, _i32, _i32, _vp, _vp]),
-            "pa_bm_destroy": (None, [_vp]),
-            "pa_bm_add_sequence": (ctypes.c_int, [_vp, _i64, _i64, _vp]),
-            "pa_bm_append": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _P32]),
-            "pa_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
-            "pa_bm_free": (ctypes.c_int, [_vp, _i64]),
-            "pa_bm_blocks_needed": (_i64, [_vp, _i64, _i64]),
-            "pa_bm_seq_info": (ctypes.c_int, [_vp, _i64, _P64, _P32, _P32, _P64, _P64]),
-            "pa_bm_table": (ctypes.c_int, [_vp, _i64, _vp, _i32]),
-            "pa_bm_block_tables": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp]),
-            "pa_bm_refcount": (_i32, [_vp, _i32, _i32]),
-            "pa_bm_preempt_latest": (ctypes.c_int, [_vp, _i32, _i64, _P64, _vp, _i32, _P32]),
-            "pa_bm_swap_in_earliest": (ctypes.c_int, [_vp, _P64, _vp, _i32, _P32]),
-            "pa_bm_resume_recompute": (ctypes.c_int, [_vp, _i64]),
-            "pa_bm_request_members": (ctypes.c_int, [_vp, _i64, _vp, _i32, _P32]),
-            "pa_bm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(_Stats)]),
-            "pa_bm_last_error": (ctypes.c_char_p, []),
-        }
-        for name, (res, args) in sig.items():
-            f = getattr(lib, name)
-            f.restype = res
-            f.argtypes = args
-        _LIB = lib
+        _LIB = _bind(ops.load_library())
     return _LIB
+
+
+def use_library(path: str) -> None:
+    """Bind the block manager to another build of block_manager.cpp (for example one built
+    with host sanitizers); it must export the pa_bm_* functions of block_manager.h."""
+    global _LIB
+    _LIB = _bind(ctypes.CDLL(path))
 
 
 def _ptr(a: Optional[np.ndarray]):
