@@ -610,8 +610,10 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (!supported_group(g))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: %d query heads per kv head "
                 "(supported: 1,2,4,8)", g);
-  // one workgroup of 256 lanes per (chunk, row tile of 128 rows, kv head)
-  const int64_t tiles_max = (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 127) / 128;
+  // one workgroup of 512 lanes per (chunk, row tile of 256 rows, kv head); rows are
+  // (token, query head) pairs
+  const int64_t tiles_max =
+      (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 255) / 256;
   if (static_cast<int64_t>(num_chunks) * tiles_max * num_kv_heads > (int64_t{1} << 24))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: grid too large");
   PA_CHECK_CONTENTS("pa_prefill_chunk",
