@@ -157,8 +157,15 @@ __device__ __forceinline__ void prefill_item(
     const int rows = max(0, min(kBlock, L - first));
     const int phys = lb < nblk ? wave_uniform(table[lb]) : 0;
     const bf16_t* src = stage_pool + (static_cast<size_t>(phys) * num_kv_heads + kvh) * slab;
+    // the descriptor's fields are uniform by construction; saying so keeps it in scalar
+    // registers (otherwise the compiler wraps every load in a loop over distinct descriptors)
+    const uint64_t sa = reinterpret_cast<uint64_t>(src);
+    const uint64_t su =
+        (static_cast<uint64_t>(static_cast<uint32_t>(wave_uniform(static_cast<int>(sa >> 32))))
+         << 32) |
+        static_cast<uint32_t>(wave_uniform(static_cast<int>(sa)));
     __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t*>(src), 0, rows * kRowBytes, kRsrcWord3);
+        reinterpret_cast<bf16_t*>(su), 0, wave_uniform(rows * kRowBytes), kRsrcWord3);
     uint4* dst = (stage_v ? vdst : kdst) + stage_blk * kBlock * kChunks;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
