@@ -135,6 +135,20 @@ def achievable_read_gbps(gib: int = 4, grids=(1024, 2048, 8192), steps: int = 20
     return best
 
 
+def achievable_mfma_tflops(iters: int = 4000, steps: int = 5) -> float:
+    """Dense bf16 MFMA rate of the library's matrix-core probe (two 512-lane workgroups per CU,
+    four independent 32x32x16 accumulation chains per wave, no memory traffic)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 2 * cus
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device="cuda")
+    ms, _ = time_calls(lambda: ops.pa_mfma_probe(sink, wgs, iters), steps, 2)
+    flops = 2.0 * 32 * 32 * 16 * 4 * iters * (wgs * 512 // 64)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"matrix-core probe, {wgs} workgroups: {ms * 1e3:.1f} us -> {tflops:.0f} TFLOP/s bf16")
+    del sink
+    return tflops
+
+
 def i32(a):
     return ops.to_device_index(a, "cuda", torch.int32)
 
@@ -487,6 +501,7 @@ def main():
     del b
     torch.cuda.empty_cache()
     achievable = achievable_read_gbps()
+    achievable_mfma = achievable_mfma_tflops()
 
     extra = {}
     if "mixed" not in skip:
@@ -538,6 +553,9 @@ def main():
         result[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
     if "mixed_batch" in extra:
         result["mixed_batch_tokens_per_s"] = round(extra["mixed_batch"]["tokens_per_s"], 1)
+        mb = result["mixed_batch"]
+        mb["achievable_mfma_tflops"] = round(achievable_mfma, 1)
+        mb["prefill_frac_of_achievable_mfma"] = round(mb["prefill_tflops"] / achievable_mfma, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

@@ -285,6 +285,16 @@ pa_status swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* s
 pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
                             int32_t num_workgroups, void* stream);
 
+/*
+ * pa_mfma_probe - a diagnostic, not part of the paged path: on `num_workgroups` workgroups of 512
+ * lanes, every wave runs `iters` rounds of four independent bf16 32x32x16 matrix-core
+ * accumulations on register operands (2 * 32 * 32 * 16 * 4 * iters flops per wave, no memory
+ * traffic) and writes one value per lane to `sink` (num_workgroups * 512 floats, device).
+ * Timing it gives the achievable dense bf16 MFMA rate that prefill is compared against.
+ * num_workgroups in [1, 2^20], iters > 0.
+ */
+pa_status pa_mfma_probe(float* sink, int32_t num_workgroups, int32_t iters, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* pa_status_string(pa_status s);
 

@@ -754,4 +754,13 @@ pa_status pa_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
                        "pa_hbm_read_probe launch");
 }
 
+pa_status pa_mfma_probe(float* sink, int32_t num_workgroups, int32_t iters, void* stream) {
+  if (!sink) return fail(PA_ERR_INVALID_ARGUMENT, "pa_mfma_probe: null pointer");
+  if (num_workgroups <= 0 || num_workgroups > (1 << 20) || iters <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_mfma_probe: num_workgroups or iters out of range");
+  return device_status(pa::launch_mfma_probe(sink, num_workgroups, iters,
+                                             static_cast<hipStream_t>(stream)),
+                       "pa_mfma_probe launch");
+}
+
 }  // extern "C"

@@ -45,4 +45,45 @@ hipError_t launch_hbm_probe(const void* src, size_t bytes, uint32_t* sink, int n
   return hipGetLastError();
 }
 
+// Matrix-core probe: the achievable dense bf16 MFMA rate on this GPU under load, measured with
+// the instruction the prefill and shared-prefix kernels use (v_mfma_f32_32x32x16_bf16).  Every
+// wave of 512-lane workgroups runs `iters` rounds of four independent accumulation chains on
+// register operands (no memory traffic), then writes one folded value per lane to `sink`.  Not
+// part of the paged path; the benchmark reports prefill MFMA rates against it beside the
+// published peak.
+constexpr int kMfmaProbeThreads = 512;
+constexpr int kMfmaProbeChains = 4;
+
+__global__ __launch_bounds__(kMfmaProbeThreads) void mfma_probe_kernel(float* __restrict__ sink,
+                                                                        int iters) {
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(1e-3f * static_cast<float>((threadIdx.x + i) & 63));
+    b[i] = static_cast<__bf16>(2e-3f * static_cast<float>(i));
+  }
+  f32x16_t acc[kMfmaProbeChains];
+#pragma unroll
+  for (int c = 0; c < kMfmaProbeChains; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kMfmaProbeChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMfmaProbeChains; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[c][v];
+  sink[static_cast<size_t>(blockIdx.x) * kMfmaProbeThreads + threadIdx.x] = s;
+}
+
+hipError_t launch_mfma_probe(float* sink, int num_workgroups, int iters, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(num_workgroups), dim3(kMfmaProbeThreads), 0, stream,
+                     sink, iters);
+  return hipGetLastError();
+}
+
 }  // namespace pa

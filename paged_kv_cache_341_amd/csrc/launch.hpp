@@ -121,5 +121,6 @@ hipError_t launch_append(const AppendArgs& a);
 hipError_t launch_cow(const CowArgs& a);
 hipError_t launch_hbm_probe(const void* src, size_t bytes, uint32_t* sink, int num_workgroups,
                             hipStream_t stream);
+hipError_t launch_mfma_probe(float* sink, int num_workgroups, int iters, hipStream_t stream);
 
 }  // namespace pa

@@ -28,7 +28,7 @@ EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_grouped",
             "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
             "pa_last_error", "pa_hbm_read_probe", "swap_blocks", "pa_set_checked_mode",
-            "pa_checked_mode")
+            "pa_checked_mode", "pa_mfma_probe")
 # the native block manager (include/block_manager.h), bound in native_block_manager.py
 BM_EXPORTED = ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_append",
                "pa_bm_fork", "pa_bm_free", "pa_bm_blocks_needed", "pa_bm_seq_info",
@@ -108,6 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swap_blocks.argtypes = [_vp] * 5 + [_i32] * 6 + [ctypes.c_int, _vp]
     lib.pa_hbm_read_probe.restype = ctypes.c_int
     lib.pa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
+    lib.pa_mfma_probe.restype = ctypes.c_int
+    lib.pa_mfma_probe.argtypes = [_vp, _i32, _i32, _vp]
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_set_checked_mode.restype = ctypes.c_int
@@ -379,6 +381,14 @@ def set_checked_mode(enable: bool) -> bool:
 
 def checked_mode() -> bool:
     return bool(load_library().pa_checked_mode())
+
+
+def pa_mfma_probe(sink: torch.Tensor, num_workgroups: int, iters: int, stream=None) -> None:
+    """Diagnostic: matrix-core loop of num_workgroups x 512 lanes (see pagedattn.h)."""
+    lib = load_library()
+    _need(sink.dtype == torch.float32 and sink.numel() >= num_workgroups * 512,
+          "sink must hold num_workgroups * 512 floats")
+    _check(lib.pa_mfma_probe(_ptr(sink), int(num_workgroups), int(iters), _stream(sink, stream)))
 
 
 def status_string(status: int) -> str:
