@@ -51,12 +51,33 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_calls(fn, steps: int, warmup: int):
+# Untimed back-to-back calls, in ms of wall time, before the warmup steps of every timed
+# region.  After an idle gap (process start, input generation, another workload's set-up) the
+# first few hundred decode calls run 2-4% slower than the steady state; 50 warmup calls alone
+# (4 ms) do not reach it, about 250 ms of continuous calls do.
+PREWARM_MS = 300.0
+
+
+def prewarm(fn, ms: float):
+    """Call fn back to back for about `ms` ms of wall time (untimed).  The queue is drained
+    every 64 calls to check the clock, so the device idles only for those short gaps."""
+    if ms <= 0:
+        return
+    end = time.perf_counter() + ms * 1e-3
+    while time.perf_counter() < end:
+        for _ in range(64):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_calls(fn, steps: int, warmup: int, prewarm_ms: float | None = None):
     """Time `steps` back-to-back calls of fn on the current stream (the stream every binding
-    launches on) with two HIP events around the whole region.  Returns (ms per call, region ms).
-    Per-call event pairs are not used: they would count host launch latency whenever the
-    device drains the queue faster than Python refills it."""
+    launches on) with two HIP events around the whole region, after a pre-warm of
+    `prewarm_ms` (default PREWARM_MS) and `warmup` untimed calls.  Returns (ms per call,
+    region ms).  Per-call event pairs are not used: they would count host launch latency
+    whenever the device drains the queue faster than Python refills it."""
     stream = torch.cuda.current_stream()
+    prewarm(fn, PREWARM_MS if prewarm_ms is None else prewarm_ms)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -466,6 +487,7 @@ def cpu_baseline(seconds: float = 10.0):
 
 
 def main():
+    global PREWARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -478,7 +500,10 @@ def main():
                     help="also time the mixed step with chunks and decodes on two streams")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain MIB-MiB device copy (for scaling rocprofv3 counters)")
+    ap.add_argument("--prewarm-ms", type=float, default=PREWARM_MS,
+                    help="untimed back-to-back calls (ms of wall time) before each timed region")
     args = ap.parse_args()
+    PREWARM_MS = max(0.0, args.prewarm_ms)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged path is "
               "built and measured on a single MI355X.", file=sys.stderr)
@@ -529,6 +554,7 @@ def main():
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "prewarm_ms": PREWARM_MS,
         "ms_per_step": round(dec["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
