@@ -36,15 +36,17 @@ METRIC = "paged decode KV GB/s (% HBM peak) + mixed-batch tokens/s at 1 MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 
-# HBM bytes per launch of pa_decode_split_kernel on decode_bf16, from two rocprofv3 passes
-# (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a plain 1 GiB copy; the summary is in
-# profiles/pa_decode.all_decode_workloads.md).  They describe the kernel source with this
-# SHA-256 prefix only (pa_decode.hip and decode_item.hpp together); after any change to them
-# the figure is reported as null.
+# HBM bytes of one pa_decode call on decode_bf16 (split kernel plus merge kernel, the same unit
+# the headline times), from two rocprofv3 passes (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a
+# plain 1 GiB copy; the summary is in profiles/pa_decode.all_decode_workloads.md).  They describe
+# the kernel source with this SHA-256 prefix only (pa_decode.hip and decode_item.hpp together);
+# after any change to them the figure is reported as null.
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_341_amd", "csrc", f)
                for f in ("pa_decode.hip", "decode_item.hpp")]
-MEASURED_TRAFFIC = {"sha256_prefix": "97eb7f0369c61c1f", "fetch_kib": 243635.7,
-                    "write_kib": 4307.8, "fetch_scale": 2.0, "write_scale": 1.0}
+MEASURED_TRAFFIC = {"sha256_prefix": "97eb7f0369c61c1f",
+                    "split": {"fetch_kib": 243635.7, "write_kib": 4307.8},
+                    "merge": {"fetch_kib": 4192.5, "write_kib": 456.0},
+                    "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def log(msg: str) -> None:
@@ -126,7 +128,8 @@ def copy_calibration(mib: int, steps: int = 10) -> None:
 
 
 def measured_traffic():
-    """HBM bytes per decode_bf16 split launch from the counters, or None if the kernel changed."""
+    """HBM bytes per decode_bf16 pa_decode call (split + merge) from the counters, or None if
+    the kernel source changed since they were taken."""
     h = hashlib.sha256()
     for p in DECODE_SRCS:
         with open(p, "rb") as f:
@@ -135,7 +138,9 @@ def measured_traffic():
     m = MEASURED_TRAFFIC
     if sha != m["sha256_prefix"]:
         return None
-    return int(1024 * (m["fetch_kib"] * m["fetch_scale"] + m["write_kib"] * m["write_scale"]))
+    kib = sum(m[k]["fetch_kib"] * m["fetch_scale"] + m[k]["write_kib"] * m["write_scale"]
+              for k in ("split", "merge"))
+    return int(1024 * kib)
 
 
 def achievable_read_gbps(gib: int = 4, grids=(1024, 2048, 8192), steps: int = 20) -> float:
