@@ -46,9 +46,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // accesses with explicit waits (wait_vmcnt_fence, lgkm_fence).  The memory clobber keeps the
 // compiler from moving LDS accesses across it.  The vector-memory counter it raises only makes
 // the compiler's own counted waits stricter, never looser.
+// The load is non-temporal (nt): every tile it stages is read once per call.  Measured on the
+// beam batch's shared prefix, the grouped call takes 80-81 us instead of 137-139 us when the
+// caches were just filled with other, dirty data, and the same (73-74 us) when they were not.
 __device__ __forceinline__ void buffer_to_lds16_untracked(__amdgpu_buffer_rsrc_t rsrc,
                                                           uint32_t lds_addr, int byte_offset) {
-  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
                :
                : "v"(byte_offset), "s"(lds_addr), "s"(rsrc)
                : "memory", "m0");
