@@ -91,10 +91,26 @@ def softmax_weights(x: np.ndarray) -> np.ndarray:
     return w / np.sum(w, axis=-1, keepdims=True)
 
 
-def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
-    """Scaled dot-product attention of query rows q [..., D] over K, V [L, D] (fp64)."""
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+           visible=None) -> np.ndarray:
+    """Scaled dot-product attention of query rows q [..., D] over K, V [L, D] (fp64).
+
+    ``visible`` (optional, bool, broadcast against the scores [..., L]) names the keys each row
+    may see; the others get score -inf, i.e. weight exactly 0.  Every row must see a key.
+    """
     x = scale * (q @ K.T)
+    if visible is not None:
+        x = np.where(visible, x, -np.inf)
     return softmax_weights(x) @ V
+
+
+def selected(count: int, wanted=None, first: int = 0) -> list:
+    """Indices i in [0, count) whose global index first + i is wanted (all when wanted is None).
+    The oracle computes only those rows; the rest of its output stays NaN."""
+    if wanted is None:
+        return list(range(count))
+    w = set(int(x) for x in wanted)
+    return [i for i in range(count) if first + i in w]
 
 
 # ---------------------------------------------------------------------------------- gathering
@@ -116,9 +132,11 @@ def gather_tokens(cache: np.ndarray, table_row: np.ndarray, length: int,
 # ----------------------------------------------------------------------------------- decoding
 def decode_ref(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype: str,
                block_size: int = 16, seqs=None) -> np.ndarray:
-    """fp64 decode output [S, Hq, D] (rows of unselected sequences are left NaN).
+    """fp64 decode output [S, Hq, D].
 
     q [S, Hq, D]; k_cache, v_cache [NB, Hkv, B, D]; block_tables int [S, MB]; seq_lens [S].
+    ``seqs`` (optional) restricts the work to those sequence indices; the rows of the others
+    stay NaN.
     """
     q = np.asarray(q)
     S, Hq, D = q.shape
@@ -127,7 +145,7 @@ def decode_ref(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype:
         raise OracleInputError("num_q_heads must be a multiple of num_kv_heads")
     sc = scale_f64(scale)
     out = np.full((S, Hq, D), np.nan)
-    for s in (range(S) if seqs is None else seqs):
+    for s in selected(S, seqs):
         L = int(seq_lens[s])
         K = to_f64(gather_tokens(k_cache, block_tables[s], L, block_size), dtype)
         V = to_f64(gather_tokens(v_cache, block_tables[s], L, block_size), dtype)
@@ -136,16 +154,6 @@ def decode_ref(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype:
             g = kv_head_of(h, Hq, Hkv)
             out[s, h] = attend(qs[h], K[:, g, :], V[:, g, :], sc)
     return out
-
-
-def decode_row_ref(q_row, k_cache, v_cache, table_row, seq_len: int, scale: float, dtype: str,
-                   head: int, num_q_heads: int, block_size: int = 16) -> np.ndarray:
-    """One (sequence, query head) decode output [D] in fp64 (for sampled checks at full size)."""
-    Hkv = k_cache.shape[1]
-    g = kv_head_of(head, num_q_heads, Hkv)
-    K = to_f64(gather_tokens(k_cache[:, g:g + 1], table_row, seq_len, block_size), dtype)[:, 0]
-    V = to_f64(gather_tokens(v_cache[:, g:g + 1], table_row, seq_len, block_size), dtype)[:, 0]
-    return attend(to_f64(q_row, dtype), K, V, scale_f64(scale))
 
 
 # ------------------------------------------------------------------------------ prefill chunks
@@ -165,7 +173,6 @@ def prefill_ref(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, sc
     qsl = np.asarray(query_start_loc, dtype=np.int64)
     if qsl[0] != 0 or qsl[-1] != T or np.any(np.diff(qsl) < 0):
         raise OracleInputError("query_start_loc must rise from 0 to total_q")
-    want = None if rows is None else set(int(r) for r in rows)
     sc = scale_f64(scale)
     out = np.full((T, Hq, D), np.nan)
     for c in range(len(qsl) - 1):
@@ -176,18 +183,19 @@ def prefill_ref(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, sc
         prefix = L - n
         if prefix < 0:
             raise OracleInputError("chunk longer than its sequence")
-        idx = [i for i in range(n) if want is None or int(qsl[c]) + i in want]
+        idx = selected(n, rows, first=int(qsl[c]))
         if not idx:
             continue
         K = to_f64(gather_tokens(k_cache, block_tables[c], L, block_size), dtype)
         V = to_f64(gather_tokens(v_cache, block_tables[c], L, block_size), dtype)
-        for i in idx:
-            r = int(qsl[c]) + i
-            nk = visible_keys(prefix + i)
-            qr = to_f64(q[r], dtype)
-            for h in range(Hq):
-                g = kv_head_of(h, Hq, Hkv)
-                out[r, h] = attend(qr[h], K[:nk, g, :], V[:nk, g, :], sc)
+        r = int(qsl[c]) + np.asarray(idx)
+        # row i (at position prefix + i) sees keys 0 .. prefix + i
+        nk = np.array([visible_keys(prefix + i) for i in idx])
+        visible = np.arange(L)[None, :] < nk[:, None]
+        qc = to_f64(q[r], dtype)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            out[r, h] = attend(qc[:, h], K[:, g, :], V[:, g, :], sc, visible)
     return out
 
 

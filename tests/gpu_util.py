@@ -42,10 +42,15 @@ def dev_i64(a, device="cuda"):
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float, what: str) -> None:
+    """Every element of `got` within atol + rtol * |ref| of `ref`.  Every reference element must
+    be a number: a NaN in `ref` means the oracle skipped an element the caller asked for, and
+    fails here rather than shrinking the comparison."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
-    mask = ~np.isnan(ref)
-    g, r = got[mask], ref[mask]
-    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    assert ref.size > 0, f"{what}: nothing to compare"
+    assert np.all(np.isfinite(ref)), f"{what}: {int(np.sum(~np.isfinite(ref)))} reference " \
+                                     f"elements are not finite (rows the oracle did not compute)"
+    g, r = got.ravel(), ref.ravel()
+    assert np.all(np.isfinite(g)), f"{what}: {int(np.sum(~np.isfinite(g)))} non-finite outputs"
     err = np.abs(g - r)
     bound = atol + rtol * np.abs(r)
     bad = err > bound
@@ -53,77 +58,156 @@ def assert_close(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float, wha
     say(f"  {what}: max|err|={err.max():.3e} max rel={np.max(err / np.maximum(np.abs(r), 1e-30)):.3e}"
         f" elements={g.size}")
     assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, worst {err[i]:.3e} " \
-                          f"vs bound {bound[i]:.3e} (ref {r[i]:.4f})"
+                          f"vs bound {bound[i]:.3e} (ref {r[i]:.4f}, flat index {i})"
+
+
+class Guarded:
+    """A device buffer of `nbytes` with `pad` canary bytes on each side.  The inside starts as
+    0xFF bytes (NaN in bf16 and fp32, so an element no kernel wrote shows up as non-finite);
+    check() asserts that no byte of either guard region changed."""
+
+    CANARY = 0xA5
+
+    def __init__(self, nbytes: int, pad: int = 4096, device="cuda"):
+        self.n, self.pad = int(nbytes), pad
+        self.buf = torch.full((self.n + 2 * pad,), self.CANARY, dtype=torch.uint8, device=device)
+        self.buf[pad:pad + self.n].fill_(0xFF)
+
+    def bytes(self) -> torch.Tensor:
+        return self.buf[self.pad:self.pad + self.n]
+
+    def tensor(self, shape, dtype) -> torch.Tensor:
+        return self.bytes().view(dtype).view(tuple(shape))
+
+    def check(self, what: str) -> None:
+        torch.cuda.synchronize()
+        head = self.buf[:self.pad]
+        tail = self.buf[self.pad + self.n:]
+        assert bool((head == self.CANARY).all()), f"{what}: bytes written before the buffer"
+        assert bool((tail == self.CANARY).all()), f"{what}: bytes written past the buffer"
+
+
+def guarded_like(t: torch.Tensor) -> Guarded:
+    return Guarded(t.numel() * t.element_size(), device=t.device)
 
 
 def run_decode(batch, max_seq_len=None, device="cuda", out=None):
-    """pa_decode on a workloads.DecodeBatch (tensors already on `device`)."""
+    """pa_decode on a workloads.DecodeBatch (tensors already on `device`).  Unless `out` is
+    given, the output and the workspace sit between canary guard regions that are checked
+    after the call."""
     msl = int(batch.seq_lens.max()) if max_seq_len is None else int(max_seq_len)
     checks.check_tables(batch.block_tables, batch.seq_lens, batch.k_cache.shape[0],
                         batch.block_size, msl)
     bt = dev_i32(batch.block_tables, device)
     sl = dev_i32(batch.seq_lens, device)
-    out = torch.empty_like(batch.q) if out is None else out
-    ops.pa_decode(out, batch.q, batch.k_cache, batch.v_cache, bt, sl, msl, batch.scale)
+    guards = []
+    if out is None:
+        g = guarded_like(batch.q)
+        out = g.tensor(batch.q.shape, batch.q.dtype)
+        guards.append(("decode out", g))
+    n = ops.pa_decode_workspace_size(batch.num_seqs, batch.num_q_heads, batch.num_kv_heads,
+                                     batch.head_dim, batch.block_size, msl)
+    ws = None
+    if n:
+        gw = Guarded(n, device=device)
+        ws = gw.bytes()
+        guards.append(("decode workspace", gw))
+    ops.pa_decode(out, batch.q, batch.k_cache, batch.v_cache, bt, sl, msl, batch.scale,
+                  workspace=ws)
+    for what, g in guards:
+        g.check(what)
     return out
 
 
 def run_decode_grouped(batch, group_start, shared_blocks, max_group_size, max_seq_len=None,
                        device="cuda", out=None, workspace=None):
-    """pa_decode_grouped on a workloads.DecodeBatch with a group plan."""
+    """pa_decode_grouped on a workloads.DecodeBatch with a group plan; output and workspace
+    guarded as in run_decode unless the caller passes them."""
     msl = int(batch.seq_lens.max()) if max_seq_len is None else int(max_seq_len)
     checks.check_tables(batch.block_tables, batch.seq_lens, batch.k_cache.shape[0],
                         batch.block_size, msl)
     checks.check_groups(group_start, shared_blocks, batch.block_tables, batch.seq_lens,
                         batch.block_size, max_group_size)
-    out = torch.empty_like(batch.q) if out is None else out
+    guards = []
+    if out is None:
+        g = guarded_like(batch.q)
+        out = g.tensor(batch.q.shape, batch.q.dtype)
+        guards.append(("grouped out", g))
+    if workspace is None:
+        n = ops.pa_decode_grouped_workspace_size(batch.num_seqs, batch.num_q_heads,
+                                                 batch.num_kv_heads, batch.head_dim,
+                                                 batch.block_size, msl)
+        gw = Guarded(n, device=device)
+        workspace = gw.bytes()
+        guards.append(("grouped workspace", gw))
     ops.pa_decode_grouped(out, batch.q, batch.k_cache, batch.v_cache,
                           dev_i32(batch.block_tables, device), dev_i32(batch.seq_lens, device),
                           dev_i32(group_start, device), dev_i32(shared_blocks, device),
                           int(max_group_size), msl, batch.scale, workspace=workspace)
+    for what, g in guards:
+        g.check(what)
     return out
 
 
 def run_mixed_step(m, device="cuda", workspace=None):
     """pa_mixed_step on a workloads.MixedStep: append, chunks and decodes in one call.  Returns
-    (chunk_out, dec_out)."""
+    (chunk_out, dec_out).  Outputs, and the workspace unless the caller passes one, sit between
+    canary guard regions that are checked after the call."""
     nb = m.k_cache.shape[0]
     checks.check_slots(m.slot_mapping, nb, m.block_size)
     C = m.chunk_seq_lens.shape[0]
     chunk_out = dec_out = None
     kw = {}
+    guards = []
     if C:
         mq = int(np.diff(m.query_start_loc).max())
         msl = int(m.chunk_seq_lens.max())
         checks.check_tables(m.chunk_tables, m.chunk_seq_lens, nb, m.block_size, msl)
         checks.check_chunks(m.query_start_loc, m.chunk_seq_lens, m.q_chunk.shape[0], mq)
-        chunk_out = torch.empty_like(m.q_chunk)
+        g = guarded_like(m.q_chunk)
+        chunk_out = g.tensor(m.q_chunk.shape, m.q_chunk.dtype)
+        guards.append(("mixed chunk out", g))
         kw.update(chunk_out=chunk_out, chunk_q=m.q_chunk,
                   chunk_tables=dev_i32(m.chunk_tables, device),
                   chunk_seq_lens=dev_i32(m.chunk_seq_lens, device),
                   query_start_loc=dev_i32(m.query_start_loc, device), chunk_max_q_len=mq,
                   chunk_max_seq_len=msl)
     S = m.decode_seq_lens.shape[0]
+    dmsl = 1
     if S:
         dmsl = int(m.decode_seq_lens.max())
         checks.check_tables(m.decode_tables, m.decode_seq_lens, nb, m.block_size, dmsl)
-        dec_out = torch.empty_like(m.q_decode)
+        g = guarded_like(m.q_decode)
+        dec_out = g.tensor(m.q_decode.shape, m.q_decode.dtype)
+        guards.append(("mixed decode out", g))
         kw.update(dec_out=dec_out, dec_q=m.q_decode, dec_tables=dev_i32(m.decode_tables, device),
                   dec_seq_lens=dev_i32(m.decode_seq_lens, device), dec_max_seq_len=dmsl)
+    if workspace is None:
+        n = ops.pa_mixed_workspace_size(S, m.num_q_heads, m.num_kv_heads, m.head_dim,
+                                        m.block_size, dmsl)
+        gw = Guarded(n, device=device)
+        workspace = gw.bytes()
+        guards.append(("mixed workspace", gw))
     ops.pa_mixed_step(m.k_cache, m.v_cache, m.scale, k_new=m.k_new, v_new=m.v_new,
                       slot_mapping=dev_i64(m.slot_mapping, device), workspace=workspace, **kw)
+    for what, g in guards:
+        g.check(what)
     return chunk_out, dec_out
 
 
 def run_prefill(q, k_cache, v_cache, tables, seq_lens, qsl, scale, device="cuda"):
+    """pa_prefill_chunk with host checks of every index input; the output sits between canary
+    guard regions that are checked after the call."""
     total_q = q.shape[0]
     max_q = int(np.diff(qsl).max())
     msl = int(np.asarray(seq_lens).max())
     checks.check_tables(tables, seq_lens, k_cache.shape[0], k_cache.shape[2], msl)
     checks.check_chunks(qsl, seq_lens, total_q, max_q)
-    out = torch.empty_like(q)
+    g = guarded_like(q)
+    out = g.tensor(q.shape, q.dtype)
     ops.pa_prefill_chunk(out, q, k_cache, v_cache, dev_i32(tables, device),
                          dev_i32(seq_lens, device), dev_i32(qsl, device), max_q, msl, scale)
+    g.check("prefill out")
     return out
 
 

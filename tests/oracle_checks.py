@@ -211,7 +211,11 @@ def check_sdpa(ref):
 
 def check_chunk_positions(ref):
     """Chunk row i (of n, ending a length-L sequence) equals a decode at length L - n + i + 1
-    (S10), and it ignores later keys while seeing every prefix key."""
+    (S10), and it ignores later keys while seeing every prefix key.
+
+    The chunk is evaluated as one masked product per head and the decode as one vector product
+    per row, so the two agree to fp64 rounding (1e-13 here), not bit for bit; moving the causal
+    bound by one key changes a row by about 1/L, some 1e-2 at these sizes."""
     L, n = 45, 12
     t = Tiny([L], Hq=2, Hkv=1, D=8, block_size=16, seed=101)
     qc = _rng(102).standard_normal((n, 2, 8)).astype(np.float32)
@@ -220,7 +224,7 @@ def check_chunk_positions(ref):
     for i in range(n):
         d = ref.decode_ref(qc[i:i + 1], t.kc, t.vc, t.tables, np.array([L - n + i + 1], np.int32),
                            t.scale, "f32", 16)
-        assert np.array_equal(ch[i], d[0]), i
+        assert np.max(np.abs(ch[i] - d[0])) <= 1e-13, i
     # a later key changes nothing for row 0; the first prefix key changes it
     i = 0
     kc, vc = t.kc.copy(), t.vc.copy()
@@ -357,9 +361,36 @@ def check_bf16_decode(ref):
     assert np.array_equal(f, b)
 
 
+def check_subsets(ref):
+    """Asking for a subset of rows (the full-size GPU comparisons do) computes exactly those
+    rows, each equal to the same row of the full evaluation, and leaves every other row NaN:
+    decode by sequence, chunks by packed row, including rows at chunk edges."""
+    t = Tiny([5, 16, 17, 50, 3], Hq=4, Hkv=2, D=8, block_size=4, seed=151)
+    full = t.decode(ref)
+    lens = np.asarray(t.lengths, np.int32)
+    for seqs in ([0], [4], [1, 3], [3, 1, 1], [0, 2, 4], []):
+        part = ref.decode_ref(t.q, t.kc, t.vc, t.tables, lens, t.scale, "f32", 4, seqs=seqs)
+        want = sorted(set(seqs))
+        assert np.max(np.abs(part[want] - full[want]), initial=0.0) <= 1e-13, seqs
+        rest = [s for s in range(len(lens)) if s not in want]
+        assert np.all(np.isnan(part[rest])), seqs
+    # two chunks: rows 0..5 end a 14-token sequence, rows 6..12 a 7-token one (prefix 0)
+    t2 = Tiny([14, 7], Hq=2, Hkv=1, D=8, block_size=4, seed=152)
+    qc = _rng(153).standard_normal((13, 2, 8)).astype(np.float32)
+    sl, qsl = np.array([14, 7], np.int32), np.array([0, 6, 13], np.int32)
+    full = ref.prefill_ref(qc, t2.kc, t2.vc, t2.tables, sl, qsl, t2.scale, "f32", 4)
+    assert np.all(np.isfinite(full))
+    for rows in ([0], [5], [6], [12], [5, 6], [0, 3, 7, 12], list(range(13)), []):
+        part = ref.prefill_ref(qc, t2.kc, t2.vc, t2.tables, sl, qsl, t2.scale, "f32", 4,
+                               rows=rows)
+        assert np.max(np.abs(part[rows] - full[rows]), initial=0.0) <= 1e-13, rows
+        rest = [r for r in range(13) if r not in rows]
+        assert np.all(np.isnan(part[rest])), rows
+
+
 ALL_CHECKS = [check_hand_example, check_brute_force, check_permutation,
               check_block_size_invariance, check_row_sums, check_single_token, check_zero_query,
               check_constant_values, check_needle, check_sdpa, check_chunk_positions,
               check_append_roundtrip, check_cow, check_swap, check_nan_poison,
               check_bf16_widening,
-              check_bf16_decode]
+              check_bf16_decode, check_subsets]

@@ -87,21 +87,29 @@ def test_decode_other_block_sizes(B):
 
 
 def test_decode_bf16_full_batch():
+    """The 64-sequence batch at full size, every element against the oracle; then ten more
+    calls that must each give the first call's bits (run-to-run identity)."""
     say("case: decode_bf16 full size (64 seqs, U[128,4096], 32/8, D128)")
     b = W.decode_bf16(device=DEV)
     out = run_decode(b)
     assert_close(widen(out), oracle_decode(b), ATOL, RTOL, "decode_bf16")
+    for i in range(10):
+        assert torch.equal(run_decode(b), out), f"call {i + 2} differs from call 1"
 
 
-def test_decode_long_context_sampled():
-    say("case: long_bf16 full size (32 x 32768, 16/4, D256), sampled sequences")
+def test_decode_long_context_full_size():
+    """The 32 x 32768-token batch (16/4 heads, D256) at full size: every sequence against the
+    oracle, eight at a time on host copies of only the blocks they use."""
+    say("case: long_bf16 full size (32 x 32768, 16/4, D256), every sequence")
     b = W.long_bf16(device=DEV)
     out = run_decode(b)
-    rows = [0, 13, 31]
-    kc, vc, tab = compact(b.k_cache, b.v_cache, b.block_tables, b.seq_lens, rows)
-    want = ref.decode_ref(raw(b.q[rows]), kc, vc, tab, b.seq_lens[rows], b.scale, "bf16")
-    assert_close(widen(out[rows]), want, ATOL, RTOL, "long_bf16 sampled")
-    assert torch.isfinite(out.float()).all()
+    got = widen(out)
+    for first in range(0, b.num_seqs, 8):
+        rows = list(range(first, min(first + 8, b.num_seqs)))
+        kc, vc, tab = compact(b.k_cache, b.v_cache, b.block_tables, b.seq_lens, rows)
+        want = ref.decode_ref(raw(b.q[rows]), kc, vc, tab, b.seq_lens[rows], b.scale, "bf16")
+        assert_close(got[rows], want, ATOL, RTOL, f"long_bf16 sequences {rows[0]}-{rows[-1]}")
+        del kc, vc
 
 
 @pytest.mark.parametrize("jstar", [0, 15, 16, 1023, 1024, 2998, 2999])
@@ -335,8 +343,9 @@ def test_cow_bit_exact_whole_pool():
 
 # ------------------------------------------------------------------- whole iterations
 def test_mixed_step_full_size():
-    """Full-size mixed step: append (whole pool exact), chunks and decodes (sampled rows)."""
-    say("case: mixed_bf16 full size (8x512 chunks, 192 decodes)")
+    """Full-size mixed step: append (whole pool exact), then every row of the eight chunks and
+    every one of the 192 decodes against the oracle."""
+    say("case: mixed_bf16 full size (8x512 chunks, 192 decodes), every row")
     m = W.mixed_bf16(device=DEV)
     bk, bv = raw(m.k_cache), raw(m.v_cache)
     run_append(m.k_cache, m.v_cache, m.k_new, m.v_new, m.slot_mapping)
@@ -346,22 +355,17 @@ def test_mixed_step_full_size():
     del wk, wv, bk, bv
     out = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
                       m.query_start_loc, m.scale)
-    rows = []
-    for c in range(8):
-        base = int(m.query_start_loc[c])
-        rows += [base, base + 1, base + 255, base + 510, base + 511]
     want = ref.prefill_ref(raw(m.q_chunk), kc, vc, m.chunk_tables, m.chunk_seq_lens,
-                           m.query_start_loc, m.scale, "bf16", rows=rows)
-    assert_close(widen(out)[rows], want[rows], ATOL, RTOL, "mixed chunks sampled")
+                           m.query_start_loc, m.scale, "bf16")
+    assert_close(widen(out), want, ATOL, RTOL, "mixed chunks, all 4096 rows")
     dec = W.DecodeBatch(q=m.q_decode, k_cache=m.k_cache, v_cache=m.v_cache,
                         block_tables=m.decode_tables, seq_lens=m.decode_seq_lens, scale=m.scale,
                         num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
                         dtype="bf16")
     dout = run_decode(dec)
-    seqs = list(range(0, 192, 7)) + [int(np.argmax(m.decode_seq_lens))]
     want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
-                          "bf16", seqs=seqs)
-    assert_close(widen(dout)[seqs], want[seqs], ATOL, RTOL, "mixed decodes sampled")
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, "mixed decodes, all 192")
 
 
 def test_beam_step_full_size():
@@ -486,9 +490,9 @@ def test_mixed_step_single_launch_ragged(G):
 def test_mixed_step_single_launch_full_size():
     """The full mixed iteration (8 x 512-row chunks, 192 decodes) in one pa_mixed_step call,
     twice with the same garbage-filled workspace (the counters are reset by the call): pool
-    bit-exact, chunk rows bit-identical to pa_prefill_chunk, decodes sampled against the
-    oracle, and the second call's outputs equal the first's."""
-    say("case: mixed_bf16 full size, single launch")
+    bit-exact, every chunk row and every decode against the oracle, chunk rows bit-identical to
+    pa_prefill_chunk, and the second call's outputs equal the first's."""
+    say("case: mixed_bf16 full size, single launch, every row")
     m = W.mixed_bf16(device=DEV)
     bk, bv = raw(m.k_cache), raw(m.v_cache)
     n = ops.pa_mixed_workspace_size(192, 32, 8, 128, 16, int(m.decode_seq_lens.max()))
@@ -498,13 +502,15 @@ def test_mixed_step_single_launch_full_size():
     kc, vc = raw(m.k_cache), raw(m.v_cache)
     assert np.array_equal(kc, wk) and np.array_equal(vc, wv)
     del wk, wv, bk, bv
+    want = ref.prefill_ref(raw(m.q_chunk), kc, vc, m.chunk_tables, m.chunk_seq_lens,
+                           m.query_start_loc, m.scale, "bf16")
+    assert_close(widen(cout), want, ATOL, RTOL, "mixed single-launch chunks, all 4096 rows")
     alone = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
                         m.query_start_loc, m.scale)
     assert torch.equal(cout, alone)
-    seqs = list(range(0, 192, 7)) + [int(np.argmax(m.decode_seq_lens))]
     want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
-                          "bf16", seqs=seqs)
-    assert_close(widen(dout)[seqs], want[seqs], ATOL, RTOL, "mixed single-launch decodes")
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, "mixed single-launch decodes, all 192")
     cout2, dout2 = run_mixed_step(m, workspace=ws)     # appends the same bytes again
     assert torch.equal(cout2, cout) and torch.equal(dout2, dout)
 

@@ -11,6 +11,7 @@ _orig_append = paged_ref.append_ref
 _orig_cow = paged_ref.cow_ref
 _orig_swap = paged_ref.swap_ref
 _orig_gather = paged_ref.gather_tokens
+_orig_selected = paged_ref.selected
 
 
 def _gather_ignoring_table(cache, table_row, length, block_size):
@@ -24,9 +25,14 @@ MUTATIONS = {
     "gqa_modulo_map": ("kv_head_of", lambda h, hq, hkv: h % hkv),
     "causal_excludes_self": ("visible_keys", lambda p: p),
     "causal_one_too_many": ("visible_keys", lambda p: p + 2),
-    "scale_dropped": ("attend", lambda q, K, V, s: _orig_attend(q, K, V, 1.0)),
-    "scale_squared": ("attend", lambda q, K, V, s: _orig_attend(q, K, V, s * s)),
-    "keys_used_as_values": ("attend", lambda q, K, V, s: _orig_attend(q, K, K, s)),
+    "scale_dropped": ("attend", lambda q, K, V, s, vis=None: _orig_attend(q, K, V, 1.0, vis)),
+    "scale_squared": ("attend", lambda q, K, V, s, vis=None: _orig_attend(q, K, V, s * s, vis)),
+    "keys_used_as_values": ("attend", lambda q, K, V, s, vis=None: _orig_attend(q, K, K, s, vis)),
+    "mask_ignored": ("attend", lambda q, K, V, s, vis=None: _orig_attend(q, K, V, s)),
+    "subset_shifted_by_one": ("selected", lambda n, w=None, first=0:
+                              _orig_selected(n, w, first + 1)),
+    "subset_drops_last": ("selected", lambda n, w=None, first=0: _orig_selected(n, w, first)[:-1]),
+    "subset_ignored": ("selected", lambda n, w=None, first=0: _orig_selected(n, None, first)),
     "softmax_unnormalised": ("softmax_weights",
                              lambda x: np.exp(x - np.max(x, axis=-1, keepdims=True))),
     "softmax_sign_flipped": ("softmax_weights", lambda x: _orig_softmax(-x)),
