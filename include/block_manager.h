@@ -10,9 +10,9 @@
  *   - fork shares the parent's block ids and raises their reference counts; the first write
  *     into a shared block takes a fresh block and copies (study-docs "Copy-on-write";
  *     cloudmash "Sharing blocks");
- *   - when blocks run out, the most recently arrived request is preempted first and all of
- *     its blocks go together, either swapped out to CPU memory or freed and recomputed later
- *     from its tokens so far (cloudmash, "When blocks run out");
+ *   - on exhaustion, preemption takes the newest request first and moves all of its blocks
+ *     at once: they go to the host pool, or they are dropped and the request's tokens are
+ *     run again later (cloudmash, "When blocks run out");
  *   - capacity is counted in blocks so admission can refuse early, and the manager keeps the
  *     counters the pages name: free and used blocks, allocation failures, tail waste,
  *     preemptions (llmdeepdive "PagedAttention & continuous batching", section "Concept").

@@ -89,7 +89,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
                     pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace pa_decode needs for these sizes (0 when no split is needed). */
+/* Bytes of workspace pa_decode needs for these sizes (0 when no split is needed).  Besides the
+ * sizes of the problem statement it takes num_kv_heads: the split plan sizes a split from the
+ * number of (sequence, kv head) work items, so the number of partials depends on it. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len);
 
@@ -252,9 +254,9 @@ size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t nu
                                int32_t head_dim, int32_t block_size, int32_t dec_max_seq_len);
 
 /*
- * swap_blocks - whole-block copies between two pools, for preemption by swapping: a preempted
- * request's blocks are swapped out to CPU memory and back in later, all of a sequence's blocks
- * together (cloudmash "Batching and PagedAttention", section "When blocks run out").  For each
+ * swap_blocks - whole-block copies between two pools, for preemption by swapping: every block
+ * of a preempted request moves to the host pool at once, and back to the device when the
+ * request resumes (cloudmash "Batching and PagedAttention", section "When blocks run out").  For each
  * pair p:
  *   dst_k[pairs[p][1]] = src_k[pairs[p][0]]; dst_v[pairs[p][1]] = src_v[pairs[p][0]]
  * whole blocks, exact bit copies.  Both pools have the layout of the device pool

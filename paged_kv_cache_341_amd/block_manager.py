@@ -16,10 +16,10 @@ What the pages describe, restated:
   * Capacity is countable in blocks, so admission can refuse a request early, before any work is
     done for it.  (llmdeepdive "Concept", continuous-batching paragraph.)
 
-  * When on-demand allocation runs out mid-generation, requests are served first come, first
-    served and the most recently arrived one is preempted first; its blocks are either swapped
-    out to CPU memory or freed and recomputed later from its tokens so far, and all blocks of a
-    sequence go together.  (cloudmash, "When blocks run out".)
+  * Requests are served in arrival order; when allocation runs dry mid-generation, preemption
+    takes the newest request first and moves all of its blocks at once: they go to the host
+    pool, or they are dropped and the request's tokens are run again later.  (cloudmash, "When
+    blocks run out".)
   * The counters to watch: free and used blocks, allocation failures, tail waste, preemptions.
     (llmdeepdive "Concept", metrics paragraph.)
 
