@@ -29,7 +29,8 @@
  * Ownership: the caller owns every buffer.  Device pointers must be device memory of the
  * current HIP device; `stream` is a hipStream_t (NULL = the default stream).  The library never
  * allocates or frees memory, keeps no pointer after returning, and holds no mutable global state
- * beyond the checked-mode switch below, so calls from several host threads are safe.  Every call
+ * beyond the checked-mode switch below and pa_decode_noalloc's static scratch array, so calls
+ * from several host threads are safe (pa_decode_noalloc's own sharing rule aside).  Every call
  * only enqueues work on `stream`: no host synchronisation, no device-to-host copy (except in
  * checked mode).
  *
@@ -94,6 +95,30 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * number of (sequence, kv head) work items, so the number of partials depends on it. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len);
+
+/*
+ * pa_decode_noalloc - for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation.  Same arguments (less the
+ * workspace) and the same result, bit for bit, as pa_decode, on the same kernels; the split
+ * partials go to a static device array inside the library instead of a caller workspace.
+ *
+ *   Scratch: PA_DECODE_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on that GPU until
+ *            the process ends.  The call allocates and frees nothing.
+ *   Limit:   sizes with pa_decode_workspace_size(...) > PA_DECODE_NOALLOC_SCRATCH_BYTES are
+ *            refused with PA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's array, which keeps the last call's partials;
+ *            calls that overlap on one GPU (other streams, other host threads) race and give
+ *            undefined results.  `stream` must belong to the current device.
+ *   Errors:  those of pa_decode, and PA_ERR_DEVICE if the array's address cannot be obtained on
+ *            the current device.
+ */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                            pa_dtype dtype, void* stream);
 
 /*
  * pa_decode_grouped - pa_decode for a batch whose sequences come in groups that share a

@@ -18,8 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "checked.cpp", "block_manager.cpp", "kv_copy.hip", "pa_decode.hip", "pa_decode_shared.hip",
-           "pa_prefill.hip", "pa_mixed.hip", "hbm_probe.hip"]
+SOURCES = ["api.cpp", "checked.cpp", "block_manager.cpp", "kv_copy.hip", "pa_decode.hip",
+           "pa_decode_shared.hip", "pa_prefill.hip", "pa_mixed.hip", "hbm_probe.hip",
+           "noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -12,13 +12,15 @@
 #include <string>
 
 #include "checked.hpp"
+#include "errors.hpp"
 #include "launch.hpp"
 
+namespace pa {
+
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-pa_status fail(pa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 pa_status fail(pa_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -33,6 +35,15 @@ pa_status ok() {
   g_last_error.clear();
   return PA_OK;
 }
+
+const char* last_error() { return g_last_error.c_str(); }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -113,7 +124,7 @@ const char* pa_status_string(pa_status s) {
   return "PA_ERR_UNKNOWN";
 }
 
-const char* pa_last_error(void) { return g_last_error.c_str(); }
+const char* pa_last_error(void) { return pa::last_error(); }
 
 int pa_set_checked_mode(int enable) { return pa::checked::set_enabled(enable != 0) ? 1 : 0; }
 

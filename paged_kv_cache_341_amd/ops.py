@@ -23,7 +23,7 @@ PA_DTYPE_BF16 = 1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED",
                 3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_DEVICE"}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_grouped",
+EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_grouped",
             "pa_decode_grouped_workspace_size", "pa_mixed_step", "pa_mixed_workspace_size",
             "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
@@ -82,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               _i32, _i32, _f32, ctypes.c_int, _vp, _sz, _vp]
     lib.pa_decode_workspace_size.restype = _sz
     lib.pa_decode_workspace_size.argtypes = [_i32] * 6
+    lib.pa_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _f32, ctypes.c_int, _vp]
     lib.pa_decode_grouped.restype = ctypes.c_int
     lib.pa_decode_grouped.argtypes = [_vp] * 8 + [_i32] * 10 + [_f32, ctypes.c_int, _vp, _sz,
                                                                 _vp]
@@ -183,6 +186,33 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        _ptr(seq_lens), S, Hq, Hkv, D, B, NB, block_tables.shape[1],
                        int(max_seq_len), float(scale), _dtype_code(q), _ptr(workspace),
                        ws_bytes, _stream(q, stream))
+    _check(st)
+    return out
+
+
+# Bytes of the library's static scratch behind pa_decode_noalloc (PA_DECODE_NOALLOC_SCRATCH_BYTES
+# in pagedattn.h).
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pa_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                      max_seq_len: int, scale: float, stream=None) -> torch.Tensor:
+    """pa_decode without a workspace: the split partials go to the library's static scratch
+    (see pagedattn.h).  Allocates nothing; calls that overlap on one GPU race."""
+    lib = load_library()
+    _contig(out, q, k_cache, v_cache, block_tables, seq_lens)
+    _need(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+          "block_tables and seq_lens must be int32")
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    _need(D2 == D and tuple(v_cache.shape) == tuple(k_cache.shape), "cache shape mismatch")
+    _need(tuple(out.shape) == tuple(q.shape), "out must match q")
+    _need(out.dtype == q.dtype == k_cache.dtype == v_cache.dtype, "dtypes must match")
+    st = lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_tables), _ptr(seq_lens), S, Hq, Hkv, D, B, NB,
+                               block_tables.shape[1], int(max_seq_len), float(scale),
+                               _dtype_code(q), _stream(q, stream))
     _check(st)
     return out
 

@@ -62,6 +62,25 @@ def test_decode_rejects(kw, status):
     assert ops.load_library().pa_last_error().decode().startswith("pa_decode")
 
 
+def test_decode_noalloc_refuses_sizes_beyond_its_scratch():
+    """Sizes whose split partials exceed the static scratch are refused by a host check,
+    before the library touches any device."""
+    lib = ops.load_library()
+    S, Hq, Hkv, D, msl = 4096, 64, 8, 256, 131072
+    assert ops.pa_decode_workspace_size(S, Hq, Hkv, D, 16, msl) > ops.DECODE_NOALLOC_SCRATCH_BYTES
+    st = lib.pa_decode_noalloc(P, P, P, P, P, P, S, Hq, Hkv, D, 16, 100000, msl // 16, msl, 0.1,
+                               1, None)
+    assert st == WS
+    msg = lib.pa_last_error().decode()
+    assert msg.startswith("pa_decode_noalloc") and str(ops.DECODE_NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_decode_noalloc_scratch_size_matches_header():
+    text = open(HEADERS[0]).read()
+    m = re.search(r"#define PA_DECODE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ops.DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_workspace_sizes():
     # one split: no workspace; long sequences: partials for every split
     assert ops.pa_decode_workspace_size(4, 2, 1, 64, 16, 100) == 0
