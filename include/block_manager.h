@@ -132,6 +132,68 @@ pa_bm_status pa_bm_request_members(const pa_bm* bm, int64_t request, int64_t* ou
 pa_bm_status pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out);
 const char* pa_bm_last_error(void);
 
+/*
+ * Step planner: one continuous-batching iteration at a time under a cap on the tokens a step
+ * processes.  After every step finished sequences leave and waiting prompts join; long prompts
+ * are cut into chunks spread over several steps (cloudmash "Batching and PagedAttention",
+ * section "Continuous batching"; llmdeepdive "Concept", continuous-batching paragraph).  The cap
+ * bounds how much prefill one step absorbs, which keeps the time per output token of decoding
+ * requests steady, and requests are served first come, first served (cloudmash, section
+ * "Scheduling is a policy, not just a mechanism"; llmdeepdive "Concept": maximum batch tokens).
+ *
+ * Readings where the pages are silent:
+ *   - every decoding sequence runs in every step, one token each; prompts share what is left,
+ *     max(0, cap - decodes) tokens;
+ *   - prefilling requests take tokens in arrival order, each min(its prompt tokens left, the
+ *     step's tokens left, max_chunk when max_chunk > 0); the rest of a prompt carries to the
+ *     next step; a request that cannot get blocks for its chunk ends the step's prefill (no
+ *     later arrival overtakes it); a prompt whose last chunk ran decodes from the next step on,
+ *     queued after the decodes already running, in arrival order;
+ *   - decodes take their blocks first, all or nothing: if the free blocks cannot cover every
+ *     decode's append (counted per sequence), pa_sp_step returns PA_BM_OUT_OF_BLOCKS and changes
+ *     nothing; making room (preemption) is the caller's decision;
+ *   - the step's slot mapping lists the chunks' tokens in chunk order, then one token per
+ *     decode in decode order: the layout kv_append and pa_mixed_step consume.
+ * The planner drives `bm` (pa_bm_add_sequence on a prompt's first chunk, appends after that);
+ * `bm` must outlive it, and the planner's sequences must not be changed through `bm` directly.
+ */
+typedef struct pa_sp pa_sp;
+
+/* Outputs of pa_sp_step, in caller-owned arrays with their capacities.  Needed capacities:
+ * decodes >= decoding sequences, chunks >= prefilling requests, slots >= max(decoding
+ * sequences, cap), copy pairs >= decoding + prefilling (each append copies at most one block);
+ * see pa_sp_counts.  chunk_lens are token counts; cow_pairs are (src, dst) block ids to copy on
+ * the device (cow_copy_blocks) before the slots are written. */
+typedef struct pa_sp_plan {
+  int64_t* chunk_seqs;
+  int64_t* chunk_lens;
+  int32_t chunk_capacity, num_chunks;
+  int64_t* decode_seqs;
+  int32_t decode_capacity, num_decodes;
+  int64_t* slot_mapping;
+  int32_t slot_capacity, num_slots;
+  int64_t* cow_pairs;          /* [capacity][2] */
+  int32_t cow_capacity, num_cow;
+} pa_sp_plan;
+
+/* A planner over `bm` with a cap of max_tokens_per_step tokens per step (> 0) and at most
+ * max_chunk prompt tokens per request per step (0: no limit).  NULL on a bad argument. */
+pa_sp* pa_sp_create(pa_bm* bm, int32_t max_tokens_per_step, int32_t max_chunk);
+void pa_sp_destroy(pa_sp* sp);
+
+/* Queue a new prompt of prompt_len (> 0) tokens; its sequence must not exist yet. */
+pa_bm_status pa_sp_add_request(pa_sp* sp, int64_t seq_id, int64_t prompt_len);
+
+/* A decoding sequence is done: it leaves the batch and its blocks are freed. */
+pa_bm_status pa_sp_finish(pa_sp* sp, int64_t seq_id);
+
+/* Numbers of decoding sequences and of prefilling requests (NULLs allowed). */
+pa_bm_status pa_sp_counts(const pa_sp* sp, int32_t* num_decoding, int32_t* num_prefilling);
+
+/* Plan and allocate one step (rules above).  INVALID (nothing changed) if a capacity is short;
+ * OUT_OF_BLOCKS (nothing changed) if the decodes' blocks do not fit. */
+pa_bm_status pa_sp_step(pa_sp* sp, pa_sp_plan* plan);
+
 #ifdef __cplusplus
 }
 #endif

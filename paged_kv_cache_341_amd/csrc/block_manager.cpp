@@ -464,4 +464,158 @@ pa_bm_status pa_bm_get_stats(const pa_bm* bm, pa_bm_stats* out) {
   return bm_ok();
 }
 
+// ------------------------------------------------------------------- step planner (token cap)
+// The rules are those of include/block_manager.h (pa_sp_*); step_planner.py states them in
+// Python and the two are tested against each other.
+
+}  // extern "C"
+
+struct pa_sp {
+  pa_bm* bm = nullptr;
+  int32_t max_tokens = 0;
+  int32_t max_chunk = 0;                                    // <= 0: no per-chunk limit
+  std::vector<std::pair<int64_t, int64_t>> prefilling;      // (sequence, prompt tokens left)
+  std::vector<int64_t> decoding;
+
+  bool queued(int64_t seq) const {
+    for (const auto& p : prefilling)
+      if (p.first == seq) return true;
+    return std::find(decoding.begin(), decoding.end(), seq) != decoding.end();
+  }
+};
+
+extern "C" {
+
+pa_sp* pa_sp_create(pa_bm* bm, int32_t max_tokens_per_step, int32_t max_chunk) {
+  if (!bm || max_tokens_per_step <= 0 || max_chunk < 0) {
+    bm_fail(PA_BM_INVALID, "pa_sp_create: need a manager, a positive cap and max_chunk >= 0");
+    return nullptr;
+  }
+  pa_sp* sp = new (std::nothrow) pa_sp();
+  if (!sp) {
+    bm_fail(PA_BM_INVALID, "pa_sp_create: out of host memory");
+    return nullptr;
+  }
+  sp->bm = bm;
+  sp->max_tokens = max_tokens_per_step;
+  sp->max_chunk = max_chunk;
+  bm_ok();
+  return sp;
+}
+
+void pa_sp_destroy(pa_sp* sp) { delete sp; }
+
+pa_bm_status pa_sp_add_request(pa_sp* sp, int64_t seq_id, int64_t prompt_len) {
+  if (!sp || prompt_len <= 0)
+    return bm_fail(PA_BM_INVALID, "pa_sp_add_request: a prompt holds at least one token");
+  if (sp->queued(seq_id) || sp->bm->seqs.count(seq_id))
+    return bm_fail(PA_BM_INVALID, "pa_sp_add_request: sequence %lld already exists",
+                   static_cast<long long>(seq_id));
+  sp->prefilling.emplace_back(seq_id, prompt_len);
+  return bm_ok();
+}
+
+pa_bm_status pa_sp_finish(pa_sp* sp, int64_t seq_id) {
+  if (!sp) return bm_fail(PA_BM_INVALID, "pa_sp_finish: null planner");
+  auto it = std::find(sp->decoding.begin(), sp->decoding.end(), seq_id);
+  if (it == sp->decoding.end())
+    return bm_fail(PA_BM_WRONG_STATE, "pa_sp_finish: sequence %lld is not decoding",
+                   static_cast<long long>(seq_id));
+  const pa_bm_status st = pa_bm_free(sp->bm, seq_id);
+  if (st != PA_BM_OK) return st;
+  sp->decoding.erase(it);
+  return bm_ok();
+}
+
+pa_bm_status pa_sp_counts(const pa_sp* sp, int32_t* num_decoding, int32_t* num_prefilling) {
+  if (!sp) return bm_fail(PA_BM_INVALID, "pa_sp_counts: null planner");
+  if (num_decoding) *num_decoding = static_cast<int32_t>(sp->decoding.size());
+  if (num_prefilling) *num_prefilling = static_cast<int32_t>(sp->prefilling.size());
+  return bm_ok();
+}
+
+pa_bm_status pa_sp_step(pa_sp* sp, pa_sp_plan* plan) {
+  if (!sp || !plan) return bm_fail(PA_BM_INVALID, "pa_sp_step: bad argument");
+  pa_bm* bm = sp->bm;
+  const int64_t ndec = static_cast<int64_t>(sp->decoding.size());
+  const int64_t npre = static_cast<int64_t>(sp->prefilling.size());
+  const int64_t max_slots = std::max<int64_t>(ndec, sp->max_tokens);
+  if (plan->decode_capacity < ndec || plan->chunk_capacity < npre ||
+      plan->slot_capacity < max_slots || plan->cow_capacity < ndec + npre ||
+      (ndec && !plan->decode_seqs) || (npre && (!plan->chunk_seqs || !plan->chunk_lens)) ||
+      (max_slots && !plan->slot_mapping) || ((ndec + npre) && !plan->cow_pairs))
+    return bm_fail(PA_BM_INVALID, "pa_sp_step: output capacities must cover %lld decodes, "
+                   "%lld chunks, %lld slots and %lld copy pairs",
+                   static_cast<long long>(ndec), static_cast<long long>(npre),
+                   static_cast<long long>(max_slots), static_cast<long long>(ndec + npre));
+  // the decodes' blocks first, all or nothing
+  int64_t need = 0;
+  for (int64_t sid : sp->decoding) {
+    auto it = bm->seqs.find(sid);
+    if (it == bm->seqs.end() || it->second.state != PA_BM_RUNNING)
+      return bm_fail(PA_BM_WRONG_STATE, "pa_sp_step: decoding sequence %lld is not resident",
+                     static_cast<long long>(sid));
+    need += bm->blocks_needed(it->second, 1);
+  }
+  if (need > bm->gpu.num_free())
+    return bm_fail(PA_BM_OUT_OF_BLOCKS, "pa_sp_step: the step's decodes need %lld blocks, %d "
+                   "free", static_cast<long long>(need), bm->gpu.num_free());
+  std::vector<int64_t> dec_slots(static_cast<size_t>(ndec));
+  int32_t ncow = 0;
+  for (int64_t i = 0; i < ndec; ++i) {
+    const int64_t sid = sp->decoding[static_cast<size_t>(i)];
+    int32_t np = 0;
+    bm->append(bm->seqs.at(sid), 1, &dec_slots[static_cast<size_t>(i)],
+               plan->cow_pairs + 2 * ncow, &np);
+    plan->decode_seqs[i] = sid;
+    ncow += np;
+  }
+  // then prompt chunks in arrival order, within what the cap leaves
+  int64_t left = std::max<int64_t>(0, static_cast<int64_t>(sp->max_tokens) - ndec);
+  int32_t nchunk = 0;
+  int64_t nslot = 0;
+  std::vector<size_t> done;
+  for (size_t i = 0; i < sp->prefilling.size() && left > 0; ++i) {
+    const int64_t sid = sp->prefilling[i].first;
+    const int64_t rem = sp->prefilling[i].second;
+    int64_t n = std::min(rem, left);
+    if (sp->max_chunk > 0) n = std::min<int64_t>(n, sp->max_chunk);
+    auto it = bm->seqs.find(sid);
+    if (it != bm->seqs.end()) {
+      if (it->second.state != PA_BM_RUNNING || bm->blocks_needed(it->second, n) > bm->gpu.num_free())
+        break;
+      int32_t np = 0;
+      bm->append(it->second, n, plan->slot_mapping + nslot, plan->cow_pairs + 2 * ncow, &np);
+      ncow += np;
+    } else {
+      if (bm->blocks_for(n) > bm->gpu.num_free()) break;
+      const int64_t r = bm->next_request++;
+      bm->requests[r] = {sid};
+      Seq& s = bm->seqs[sid];
+      s.request = r;
+      bm->append(s, n, plan->slot_mapping + nslot, nullptr, nullptr);
+    }
+    plan->chunk_seqs[nchunk] = sid;
+    plan->chunk_lens[nchunk] = n;
+    ++nchunk;
+    nslot += n;
+    left -= n;
+    if (n == rem) done.push_back(i);
+    else sp->prefilling[i].second = rem - n;
+  }
+  for (auto d = done.rbegin(); d != done.rend(); ++d) {
+    sp->decoding.push_back(sp->prefilling[*d].first);
+    sp->prefilling.erase(sp->prefilling.begin() + static_cast<std::ptrdiff_t>(*d));
+  }
+  // finished prompts join the decodes in arrival order
+  if (done.size() > 1)
+    std::reverse(sp->decoding.end() - static_cast<std::ptrdiff_t>(done.size()), sp->decoding.end());
+  std::copy(dec_slots.begin(), dec_slots.end(), plan->slot_mapping + nslot);
+  plan->num_chunks = nchunk;
+  plan->num_decodes = static_cast<int32_t>(ndec);
+  plan->num_slots = static_cast<int32_t>(nslot + ndec);
+  plan->num_cow = ncow;
+  return bm_ok();
+}
+
 }  // extern "C"

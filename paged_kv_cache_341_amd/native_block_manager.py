@@ -31,6 +31,15 @@ class _Stats(ctypes.Structure):
         "tail_waste_slots", "num_sequences", "num_requests")]
 
 
+class _Plan(ctypes.Structure):
+    """pa_sp_plan (block_manager.h), field for field."""
+    _fields_ = [("chunk_seqs", _vp), ("chunk_lens", _vp), ("chunk_capacity", _i32),
+                ("num_chunks", _i32), ("decode_seqs", _vp), ("decode_capacity", _i32),
+                ("num_decodes", _i32), ("slot_mapping", _vp), ("slot_capacity", _i32),
+                ("num_slots", _i32), ("cow_pairs", _vp), ("cow_capacity", _i32),
+                ("num_cow", _i32)]
+
+
 _LIB = None
 
 
@@ -53,6 +62,12 @@ def _bind(lib):
         "pa_bm_request_members": (ctypes.c_int, [_vp, _i64, _vp, _i32, _P32]),
         "pa_bm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(_Stats)]),
         "pa_bm_last_error": (ctypes.c_char_p, []),
+        "pa_sp_create": (_vp, [_vp, _i32, _i32]),
+        "pa_sp_destroy": (None, [_vp]),
+        "pa_sp_add_request": (ctypes.c_int, [_vp, _i64, _i64]),
+        "pa_sp_finish": (ctypes.c_int, [_vp, _i64]),
+        "pa_sp_counts": (ctypes.c_int, [_vp, _P32, _P32]),
+        "pa_sp_step": (ctypes.c_int, [_vp, ctypes.POINTER(_Plan)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -258,3 +273,55 @@ class NativeBlockManager:
     def resume_recompute(self, request: int) -> List[Tuple[int, int]]:
         self._check(_lib().pa_bm_resume_recompute(self._h, int(request)))
         return [(s, self.recompute_tokens(s)) for s in self.members(request)]
+
+
+class NativeStepPlanner:
+    """The C++ step planner (pa_sp_*) behind the interface of ``step_planner.StepPlanner``:
+    add_request, finish and step() returning a ``StepPlan``."""
+
+    def __init__(self, bm: NativeBlockManager, max_tokens_per_step: int,
+                 max_chunk: Optional[int] = None):
+        lib = _lib()
+        h = lib.pa_sp_create(bm._h, int(max_tokens_per_step),
+                             0 if max_chunk is None else int(max_chunk))
+        if not h:
+            raise ValueError(lib.pa_bm_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+        self.bm = bm                      # keeps the manager alive as long as the planner
+        self.max_tokens = int(max_tokens_per_step)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _LIB is not None:
+            _LIB.pa_sp_destroy(h)
+            self._h = None
+
+    def counts(self) -> Tuple[int, int]:
+        d, p = ctypes.c_int32(), ctypes.c_int32()
+        self.bm._check(_lib().pa_sp_counts(self._h, ctypes.byref(d), ctypes.byref(p)))
+        return d.value, p.value
+
+    def add_request(self, seq_id: int, prompt_len: int) -> None:
+        self.bm._check(_lib().pa_sp_add_request(self._h, int(seq_id), int(prompt_len)))
+
+    def finish(self, seq_id: int) -> None:
+        self.bm._check(_lib().pa_sp_finish(self._h, int(seq_id)))
+
+    def step(self):
+        from .step_planner import StepPlan
+        nd, npre = self.counts()
+        cs = np.empty(max(npre, 1), np.int64)
+        cl = np.empty(max(npre, 1), np.int64)
+        ds = np.empty(max(nd, 1), np.int64)
+        ns = max(nd, self.max_tokens)
+        sm = np.empty(max(ns, 1), np.int64)
+        cp = np.empty(2 * max(nd + npre, 1), np.int64)
+        plan = _Plan(_ptr(cs), _ptr(cl), npre, 0, _ptr(ds), nd, 0, _ptr(sm), ns, 0, _ptr(cp),
+                     nd + npre, 0)
+        self.bm._check(_lib().pa_sp_step(self._h, ctypes.byref(plan)))
+        return StepPlan(chunk_seqs=cs[:plan.num_chunks].tolist(),
+                        chunk_lens=cl[:plan.num_chunks].tolist(),
+                        decode_seqs=ds[:plan.num_decodes].tolist(),
+                        slot_mapping=sm[:plan.num_slots].copy(),
+                        cow_pairs=[(int(a), int(b)) for a, b in
+                                   cp[:2 * plan.num_cow].reshape(-1, 2)])

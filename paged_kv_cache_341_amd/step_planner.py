@@ -1,0 +1,154 @@
+"""Per-step token cap for a continuous-batching iteration: which tokens one step processes.
+
+What the pages describe, restated:
+  * After every step, finished sequences leave and waiting prompts join; one step mixes the
+    prompt tokens of newly admitted requests with one new token of every decoding sequence.
+    (cloudmash "Batching and PagedAttention", section "Continuous batching"; llmdeepdive
+    "PagedAttention & continuous batching", section "Concept", continuous-batching paragraph.)
+  * Long prompts are cut into chunks spread over several steps, so that one large prefill does
+    not hold up the next token of every running sequence.  (Same sections.)
+  * Engines cap the number of tokens one step processes: the cap bounds how much prefill work a
+    step can take on, which keeps the time per output token of the decoding requests steady;
+    requests are served first come, first served.  (cloudmash, section "Scheduling is a policy,
+    not just a mechanism"; llmdeepdive "Concept": maximum batch tokens.)
+
+Readings where the pages are silent:
+  * Every decoding sequence runs in every step (one token each); the cap limits what prefill
+    may add on top, so prefill gets ``max(0, cap - decodes)`` tokens.  Decodes alone are never
+    cut: a decode is the work the cap protects.
+  * Prompt tokens go to prefilling requests in arrival order.  Each takes
+    ``min(tokens left in its prompt, tokens left in the step, max_chunk)``; what is left of its
+    prompt carries to the next step.  A request that cannot get blocks for its chunk stops the
+    prefill of this step: later arrivals do not overtake it.
+  * A prompt whose last chunk ran becomes a decoding sequence in the next step.
+  * Layout of the step's new tokens (one slot mapping, as the device append consumes it): the
+    chunks' tokens in chunk order, then one token per decode in decode order.
+  * Decodes take their blocks first.  If the pool cannot give every decode its block (counted
+    per sequence, so a block shared by forks counts once per fork that must copy it), the step
+    is refused and nothing changes: freeing room (preemption) is the caller's decision.
+
+The plan is host-side integer work only: it produces the inputs of kv_append, pa_prefill_chunk
+and pa_decode (or pa_mixed_step) and moves no KV bytes.  ``paged_kv_cache_341_amd/csrc/
+block_manager.cpp`` implements the same rules natively (pa_sp_*); the two are tested against
+each other.
+"""
+from __future__ import annotations
+
+from collections import OrderedDict
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .block_manager import RUNNING, OutOfBlocks, blocks_for
+
+
+def chunk_budget(max_tokens: int, num_decodes: int, remaining: Sequence[int],
+                 max_chunk: Optional[int] = None) -> List[int]:
+    """Prompt tokens each prefilling request (arrival order) gets in a step that runs
+    ``num_decodes`` decodes under a cap of ``max_tokens`` tokens."""
+    if max_tokens <= 0 or num_decodes < 0 or (max_chunk is not None and max_chunk <= 0):
+        raise ValueError("max_tokens and max_chunk must be positive, num_decodes >= 0")
+    left = max(0, max_tokens - num_decodes)
+    out = []
+    for r in remaining:
+        if r < 0:
+            raise ValueError("remaining prompt tokens must be >= 0")
+        n = min(int(r), left)
+        if max_chunk is not None:
+            n = min(n, max_chunk)
+        out.append(n)
+        left -= n
+    return out
+
+
+@dataclass
+class StepPlan:
+    """One step's work: the chunks (prefill) and decodes, and the device inputs for them."""
+
+    chunk_seqs: List[int] = field(default_factory=list)
+    chunk_lens: List[int] = field(default_factory=list)
+    decode_seqs: List[int] = field(default_factory=list)
+    slot_mapping: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    cow_pairs: List[Tuple[int, int]] = field(default_factory=list)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(sum(self.chunk_lens)) + len(self.decode_seqs)
+
+    def query_start_loc(self) -> np.ndarray:
+        qsl = np.zeros(len(self.chunk_lens) + 1, dtype=np.int32)
+        qsl[1:] = np.cumsum(self.chunk_lens)
+        return qsl
+
+
+class StepPlanner:
+    """Queues of decoding and prefilling sequences over a block manager (the Python
+    ``BlockManager`` or ``NativeBlockManager``: the same methods), planned one step at a time
+    under a token cap."""
+
+    def __init__(self, bm, max_tokens_per_step: int, max_chunk: Optional[int] = None):
+        if max_tokens_per_step <= 0 or (max_chunk is not None and max_chunk <= 0):
+            raise ValueError("max_tokens_per_step and max_chunk must be positive")
+        self.bm = bm
+        self.max_tokens = int(max_tokens_per_step)
+        self.max_chunk = None if max_chunk is None else int(max_chunk)
+        self.prefilling: "OrderedDict[int, int]" = OrderedDict()   # seq -> prompt tokens left
+        self.decoding: List[int] = []
+
+    def add_request(self, seq_id: int, prompt_len: int) -> None:
+        """A new prompt joins the queue (arrival order); its blocks come with its chunks."""
+        if prompt_len <= 0:
+            raise ValueError("a prompt holds at least one token")
+        if seq_id in self.prefilling or seq_id in self.decoding or self.bm.has(seq_id):
+            raise ValueError(f"sequence {seq_id} already exists")
+        self.prefilling[seq_id] = int(prompt_len)
+
+    def finish(self, seq_id: int) -> None:
+        """A decoding sequence is done: it leaves the batch and its blocks return."""
+        self.decoding.remove(seq_id)
+        self.bm.free(seq_id)
+
+    def step(self) -> StepPlan:
+        """Plan one step: append one token to every decoding sequence, then prompt chunks in
+        arrival order within the cap.  Raises OutOfBlocks, changing nothing, when the decodes'
+        blocks do not fit."""
+        bm = self.bm
+        decodes = list(self.decoding)
+        need = sum(bm.blocks_needed(s, 1) for s in decodes)
+        if need > bm.num_free:
+            raise OutOfBlocks(f"the step's decodes need {need} blocks, {bm.num_free} free")
+        plan = StepPlan(decode_seqs=decodes)
+        dec_slots: List[int] = []
+        for s in decodes:
+            sl, pairs = bm.append_tokens(s, 1)
+            dec_slots += sl
+            plan.cow_pairs += pairs
+        budget = chunk_budget(self.max_tokens, len(decodes), list(self.prefilling.values()),
+                              self.max_chunk)
+        chunk_slots: List[int] = []
+        done = []
+        for (s, left), n in zip(list(self.prefilling.items()), budget):
+            if n == 0:
+                continue
+            if bm.has(s):
+                if bm.state(s) != RUNNING or bm.blocks_needed(s, n) > bm.num_free:
+                    break
+                sl, pairs = bm.append_tokens(s, n)
+                plan.cow_pairs += pairs
+            else:
+                if blocks_for(n, bm.block_size) > bm.num_free:
+                    break
+                sl = bm.add_sequence(s, n)
+            chunk_slots += sl
+            plan.chunk_seqs.append(s)
+            plan.chunk_lens.append(n)
+            if left == n:
+                done.append(s)
+            else:
+                self.prefilling[s] = left - n
+        for s in done:
+            del self.prefilling[s]
+            self.decoding.append(s)
+        plan.slot_mapping = np.asarray(chunk_slots + dec_slots, dtype=np.int64)
+        return plan

@@ -252,6 +252,13 @@ for fn in (t.test_paged_admission_matches_page, t.test_sandbox_and_pitfall,
            t.test_copy_on_write_rules, t.test_swap_out_latest_then_back_in,
            t.test_recompute_and_protect):
     fn(t.native)
+from tests import test_step_planner as sp
+for seed in range(6):
+    sp.test_native_matches_python(seed)
+for fn in (sp.test_long_prompt_does_not_stall_decodes, sp.test_first_come_first_served_and_max_chunk,
+           sp.test_short_pool_rules):
+    fn("native", nbm.NativeBlockManager, nbm.NativeStepPlanner)
+sp.test_native_refuses_bad_arguments()
 print("sanitized run ok")
 """
 
