@@ -94,27 +94,51 @@ def time_calls(fn, steps: int, warmup: int, prewarm_ms: float | None = None):
     return total / steps, total
 
 
-def time_cold(fn, reps: int, flush_mib: int = 512):
-    """Per-call times with the caches cold: before each call a `flush_mib` MiB scratch buffer is
-    overwritten, which evicts the 4 MB L2s and the 256 MB MALL, then the call is bracketed by
-    its own pair of HIP events.  The flush keeps the device busy while the host enqueues the
-    call, so the events see no launch gap.  Returns median, p10 and p90 in ms."""
+class CacheFlush:
+    """Evicts the L2s and the 256 MB MALL with clean lines: a `mib` MiB scratch buffer is
+    overwritten (evicting whatever the caches held), then a second `mib` MiB buffer is read
+    (replacing the scratch's dirty lines, whose write-back happens here and not inside the
+    timed call that follows).  The caches then hold only clean lines of data no kernel under
+    test reads."""
+
+    def __init__(self, mib: int = 512):
+        self.write_buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+        self.read_buf = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda")
+        self.sink = None
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.write_buf.fill_(self.i & 0xFF)
+        # a reduction in the buffer's own type: it reads the buffer and writes one scalar (a
+        # widening sum would first write a converted copy of the whole buffer)
+        self.sink = self.read_buf.sum()
+
+
+def time_cold(fn, reps: int, flush: CacheFlush | None = None):
+    """Per-call times with cold caches: before each call the caches are flushed (CacheFlush),
+    then the call is bracketed by its own pair of HIP events on the stream the bindings launch
+    on.  The flush keeps the device busy while the host enqueues
+    the call, so the events see no launch gap.  Returns median, mean, p10 and p90 in ms."""
     stream = torch.cuda.current_stream()
-    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    own = flush is None
+    flush = CacheFlush() if own else flush
     fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
-    for i, (e0, e1) in enumerate(evs):
-        scratch.fill_(i & 0xFF)
+    for e0, e1 in evs:
+        flush()
         e0.record(stream)
         fn()
         e1.record(stream)
     torch.cuda.synchronize()
     t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    del scratch
-    return dict(median_ms=float(np.median(t)), p10_ms=float(np.percentile(t, 10)),
-                p90_ms=float(np.percentile(t, 90)), reps=reps)
+    if own:
+        del flush
+    return dict(median_ms=float(np.median(t)), mean_ms=float(np.mean(t)),
+                p10_ms=float(np.percentile(t, 10)), p90_ms=float(np.percentile(t, 90)),
+                reps=reps)
 
 
 def copy_calibration(mib: int, steps: int = 10) -> None:
@@ -220,18 +244,23 @@ def grouped_decode_callable(b, group_start, shared_blocks, max_group):
 
 
 def bench_decode(b, steps, warmup, name, cold_reps=0):
+    """Warm (back-to-back, after the pre-warm) and, with cold_reps, cold-cache timings of one
+    pa_decode call on batch b, with KV GB/s and fractions of the HBM peak."""
     fn = decode_callable(b)
     mean_ms, total_ms = time_calls(fn, steps, warmup)
     nbytes = kv_bytes(b.seq_lens, b.num_kv_heads, b.head_dim)
     gbps = nbytes / (mean_ms * 1e-3) / 1e9
     log(f"{name}: {mean_ms * 1e3:.1f} us/call, "
         f"{nbytes / 1e6:.1f} MB KV -> {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of HBM)")
-    res = dict(ms=mean_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps)
+    res = dict(ms=mean_ms, total_ms=total_ms, kv_bytes=nbytes, gbps=gbps,
+               frac=gbps / HBM_PEAK_GBPS)
     if cold_reps:
         c = time_cold(fn, cold_reps)
         c["gbps_median"] = nbytes / (c["median_ms"] * 1e-3) / 1e9
+        c["frac_median"] = c["gbps_median"] / HBM_PEAK_GBPS
         log(f"{name} cold caches: median {c['median_ms'] * 1e3:.1f} us (p10 "
-            f"{c['p10_ms'] * 1e3:.1f}, p90 {c['p90_ms'] * 1e3:.1f}) -> {c['gbps_median']:.0f} GB/s")
+            f"{c['p10_ms'] * 1e3:.1f}, p90 {c['p90_ms'] * 1e3:.1f}) -> {c['gbps_median']:.0f} GB/s "
+            f"({100 * c['frac_median']:.1f}% of HBM)")
         res["cold"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in c.items()}
     return res
 
@@ -323,21 +352,44 @@ def bench_mixed(steps, warmup, overlap=False):
     t_app = time_calls(append, steps, warmup)
     t_pre = time_calls(prefill, steps, warmup)
     t_dec = time_calls(dfn, steps, warmup)
+    flush = CacheFlush()
+    cold_step = time_cold(step, max(steps, 20), flush)
+    cold_pre = time_cold(prefill, max(steps, 20), flush)
+    cold_dec = time_cold(dfn, max(steps, 20), flush)
+    del flush
     T = len(m.slot_mapping)
     flops = chunk_flops(m.extra["prefixes"], np.diff(m.query_start_loc), 32, 128)
     app_bytes = 2 * T * 8 * 128 * 2 * 2          # read + write of K and V rows
     dec_bytes = kv_bytes(m.decode_seq_lens, 8, 128)
     tflops = flops / (t_pre[0] * 1e-3) / 1e12
+    tflops_cold = flops / (cold_pre["median_ms"] * 1e-3) / 1e12
+    dec_gbps = dec_bytes / (t_dec[0] * 1e-3) / 1e9
+    dec_gbps_cold = dec_bytes / (cold_dec["median_ms"] * 1e-3) / 1e9
     res = dict(
         tokens_per_s=T / (t_step[0] * 1e-3), ms_per_step=t_step[0], new_tokens=T,
-
+        tokens_per_s_cold=T / (cold_step["median_ms"] * 1e-3),
+        ms_per_step_cold=cold_step["median_ms"],
         append_ms=t_app[0], append_gbps=app_bytes / (t_app[0] * 1e-3) / 1e9,
         prefill_ms=t_pre[0], prefill_gflop=flops / 1e9, prefill_tflops=tflops,
         prefill_mfma_frac=tflops / BF16_PEAK_TFLOPS,
-        decode_ms=t_dec[0], decode_kv_bytes=dec_bytes,
-        decode_gbps=dec_bytes / (t_dec[0] * 1e-3) / 1e9,
+        prefill_cold_median_ms=cold_pre["median_ms"],
+        decode_ms=t_dec[0], decode_kv_bytes=dec_bytes, decode_gbps=dec_gbps,
+        decode_cold_median_ms=cold_dec["median_ms"],
         single_launch_ms=t_single[0], single_launch_tokens_per_s=T / (t_single[0] * 1e-3),
-        graph_replay_ms=t_graph[0], graph_replay_tokens_per_s=T / (t_graph[0] * 1e-3))
+        graph_replay_ms=t_graph[0], graph_replay_tokens_per_s=T / (t_graph[0] * 1e-3),
+        prefill_roofline={"bound": "mfma", "kernel": "pa_prefill_kernel",
+                          "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                          "achieved_cold": round(tflops_cold, 1),
+                          "frac_cold": round(tflops_cold / BF16_PEAK_TFLOPS, 4),
+                          "algorithmic_flops": flops},
+        decode_roofline={"bound": "hbm", "kernel": "pa_decode_split_kernel + "
+                                                   "pa_decode_merge_kernel",
+                         "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                         "achieved_cold": round(dec_gbps_cold, 1),
+                         "frac_cold": round(dec_gbps_cold / HBM_PEAK_GBPS, 4),
+                         "algorithmic_bytes": dec_bytes})
     if t_over is not None:
         res.update(overlapped_tokens_per_s=T / (t_over[0] * 1e-3), overlapped_ms_per_step=t_over[0])
         log(f"mixed step, chunks and decodes on two streams: {t_over[0] * 1e3:.1f} us -> "
@@ -346,6 +398,10 @@ def bench_mixed(steps, warmup, overlap=False):
         f"{t_app[0] * 1e3:.1f} us | prefill {t_pre[0] * 1e3:.1f} us {tflops:.0f} TFLOP/s "
         f"({100 * res['prefill_mfma_frac']:.1f}% MFMA) | decode {t_dec[0] * 1e3:.1f} us "
         f"{res['decode_gbps']:.0f} GB/s")
+    log(f"mixed step cold caches: {cold_step['median_ms'] * 1e3:.1f} us -> "
+        f"{res['tokens_per_s_cold']:.0f} tok/s | prefill {cold_pre['median_ms'] * 1e3:.1f} us "
+        f"{tflops_cold:.0f} TFLOP/s | decode {cold_dec['median_ms'] * 1e3:.1f} us "
+        f"{dec_gbps_cold:.0f} GB/s")
     log(f"mixed step as one pa_mixed_step call (single launch): {t_single[0] * 1e3:.1f} us -> "
         f"{res['single_launch_tokens_per_s']:.0f} tok/s")
     log(f"mixed step replayed from a HIP graph: {t_graph[0] * 1e3:.1f} us -> "
@@ -434,77 +490,122 @@ def bench_swap(steps, warmup, num_blocks=2048):
     return res
 
 
-def sweep_block_size(steps, warmup):
-    """Decode bandwidth against block size, with physical blocks scattered (a seeded random free
-    list) or laid out contiguously per sequence, on the 64-sequence batch and the long context;
-    plus the tail waste (slots allocated but holding no token) each block size costs."""
+def contiguous_callable(c):
+    seq_lens = i32(c.seq_lens)
+    out = torch.empty_like(c.q)
+    ws_n = ops.pa_decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                        16, c.max_seq_len)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        ops.pa_decode_contiguous(out, c.q, c.k, c.v, seq_lens, c.max_seq_len, c.scale,
+                                 workspace=ws)
+    return fn
+
+
+def indirection_sweep(reps: int, block_sizes=(1, 4, 8, 16, 32, 64)):
+    """The cost of paging: cold-cache decode time through the block table at each block size,
+    against the same decode over contiguous KV (pa_decode_contiguous: the same kernel walk with
+    the table taken out), on the 64-sequence batch and the long context; plus the same 16-token
+    paged decode with blocks handed out in id order (placement alone), and the tail waste each
+    block size costs."""
     res = {}
-    for name, make in (("decode_bf16", W.decode_bf16), ("long_bf16", W.long_bf16)):
-        for B in (8, 16, 32, 64):
-            row = {}
-            for scatter in (True, False):
-                b = make(device="cuda", poison=False, block_size=B, scatter=scatter)
-                r = bench_decode(b, steps, warmup, f"{name} B={B} "
-                                 f"{'scattered' if scatter else 'contiguous'}")
-                row["scattered_gbps" if scatter else "contiguous_gbps"] = round(r["gbps"], 1)
-                row["scattered_us" if scatter else "contiguous_us"] = round(r["ms"] * 1e3, 2)
-                lens = b.seq_lens.astype(np.int64)
-                row["tail_waste_frac"] = round(float(((-(-lens // B)) * B - lens).sum()
-                                                     / lens.sum()), 5)
-                del b
-                torch.cuda.empty_cache()
-            row["paged_over_contiguous_time"] = round(row["scattered_us"] / row["contiguous_us"], 4)
-            res[f"{name}/B{B}"] = row
-            log(f"  {name} B={B}: scattered {row['scattered_gbps']} GB/s, contiguous "
-                f"{row['contiguous_gbps']} GB/s, paged/contiguous time "
-                f"{row['paged_over_contiguous_time']}, tail waste {row['tail_waste_frac']}")
+    flush = CacheFlush()
+    for name, make, make_c in (("decode_bf16", W.decode_bf16, W.decode_bf16_contiguous),
+                               ("long_bf16", W.long_bf16, W.long_bf16_contiguous)):
+        c = make_c(device="cuda", poison=False)
+        nbytes = kv_bytes(c.seq_lens, c.num_kv_heads, c.head_dim)
+        ct = time_cold(contiguous_callable(c), reps, flush)
+        del c
+        torch.cuda.empty_cache()
+        row = {"contiguous_us": round(ct["median_ms"] * 1e3, 2),
+               "contiguous_gbps": round(nbytes / (ct["median_ms"] * 1e-3) / 1e9, 1)}
+        log(f"{name} contiguous KV: {row['contiguous_us']} us cold ({row['contiguous_gbps']} GB/s)")
+        for B in block_sizes:
+            b = make(device="cuda", poison=False, block_size=B)
+            pt = time_cold(decode_callable(b), reps, flush)
+            lens = b.seq_lens.astype(np.int64)
+            waste = float(((-(-lens // B)) * B - lens).sum() / lens.sum())
+            del b
+            torch.cuda.empty_cache()
+            us = pt["median_ms"] * 1e3
+            row[f"B{B}"] = {"paged_us": round(us, 2),
+                            "paged_gbps": round(nbytes / (pt["median_ms"] * 1e-3) / 1e9, 1),
+                            "paged_over_contiguous_time": round(us / row["contiguous_us"], 4),
+                            "tail_waste_frac": round(waste, 5)}
+            log(f"  {name} B={B}: paged {us:.1f} us cold, paged/contiguous time "
+                f"{us / row['contiguous_us']:.3f}, tail waste {waste:.4f}")
+        b = make(device="cuda", poison=False, block_size=16, scatter=False)
+        pt = time_cold(decode_callable(b), reps, flush)
+        del b
+        torch.cuda.empty_cache()
+        row["B16_blocks_in_id_order_us"] = round(pt["median_ms"] * 1e3, 2)
+        res[name] = row
+    del flush
     return res
 
 
-def cpu_baseline(seconds: float = 10.0):
-    """The fp64 oracle on the host cores, over whole passes of the decode batch (same generator,
-    CPU copy of the inputs) until about `seconds` have been spent."""
+def cpu_baseline(seconds: float = 10.0, single_seconds: float = 6.0):
+    """The fp64 oracle on the host cores: whole passes over the decode batch (same generator,
+    CPU copy of the inputs) with BLAS allowed every core this process may run on, until about
+    `seconds` have been spent; then the same oracle on one thread over the batch's first 16
+    sequences, until about `single_seconds` have been spent."""
     from oracle import paged_ref as ref
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
     b = W.decode_bf16(device="cpu", poison=False)
     q = b.q.view(torch.int16).numpy().view(np.uint16)
     kc = b.k_cache.view(torch.int16).numpy().view(np.uint16)
     vc = b.v_cache.view(torch.int16).numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        ref.decode_ref(q, kc, vc, b.block_tables, b.seq_lens, b.scale, "bf16")
-        passes += 1
-        if time.perf_counter() - t0 > seconds:
-            break
-    dt = time.perf_counter() - t0
-    nbytes = passes * kv_bytes(b.seq_lens, 8, 128)
-    gbps = nbytes / dt / 1e9
-    log(f"cpu oracle: {passes} passes over the decode batch in {dt:.1f} s -> {gbps:.3f} GB/s")
-    return {"value": gbps, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+
+    def run(limit, seqs, budget):
+        with threadpool_limits(limits=limit):
+            t0 = time.perf_counter()
+            passes = 0
+            while True:
+                ref.decode_ref(q, kc, vc, b.block_tables, b.seq_lens, b.scale, "bf16",
+                               seqs=seqs)
+                passes += 1
+                if time.perf_counter() - t0 > budget:
+                    break
+            dt = time.perf_counter() - t0
+        lens = b.seq_lens if seqs is None else b.seq_lens[list(seqs)]
+        return passes, dt, passes * kv_bytes(lens, 8, 128) / dt / 1e9
+
+    passes, dt, gbps = run(cores, None, seconds)
+    sample = list(range(16))
+    p1, dt1, gbps1 = run(1, sample, single_seconds)
+    log(f"cpu oracle: {passes} passes over the decode batch in {dt:.1f} s on {cores} cores -> "
+        f"{gbps:.3f} GB/s; one thread: {p1} passes over 16 sequences in {dt1:.1f} s -> "
+        f"{gbps1:.3f} GB/s")
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{passes} full passes over the 64-sequence decode batch "
                       f"({kv_bytes(b.seq_lens, 8, 128) / 1e6:.0f} MB KV each), numpy fp64, "
-                      f"{dt:.1f} s"}
+                      f"BLAS threads = {cores} (sched_getaffinity), {dt:.1f} s",
+            "single_thread": {"value": round(gbps1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"{p1} passes over the batch's first 16 sequences "
+                                        f"({kv_bytes(b.seq_lens[:16], 8, 128) / 1e6:.0f} MB KV "
+                                        f"each), {dt1:.1f} s"}}
 
 
 def main():
     global PREWARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed decode calls: cold-cache reps for the headline, and back-to-back "
+                         "calls for the warm figure")
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip", default="", help="comma list of: mixed,long,beams,swap")
-    ap.add_argument("--sweep-block-size", action="store_true",
-                    help="also sweep block sizes 8/16/32/64, scattered vs contiguous blocks")
+    ap.add_argument("--skip", default="",
+                    help="comma list of: mixed,long,beams,swap,indirection")
     ap.add_argument("--overlap-mixed", action="store_true",
                     help="also time the mixed step with chunks and decodes on two streams")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain MIB-MiB device copy (for scaling rocprofv3 counters)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only the headline's cold-cache decode calls (for a kernel trace whose "
+                         "averages are the headline's): no warm region, probes or other workloads")
     ap.add_argument("--prewarm-ms", type=float, default=PREWARM_MS,
                     help="untimed back-to-back calls (ms of wall time) before each timed region")
     args = ap.parse_args()
@@ -525,7 +626,16 @@ def main():
 
     log("workload decode_bf16 (64 seqs, lens U[128,4096], 32/8 heads, D128, bf16)")
     b = W.decode_bf16(device="cuda", poison=False)
-    dec = bench_decode(b, steps, warmup, "decode_bf16", cold_reps=100)
+    if args.cold_only:
+        c = time_cold(decode_callable(b), steps)
+        nbytes = kv_bytes(b.seq_lens, b.num_kv_heads, b.head_dim)
+        gbps = nbytes / (c["median_ms"] * 1e-3) / 1e9
+        print(json.dumps({"cold_only": True, "median_ms": round(c["median_ms"], 5),
+                          "mean_ms": round(c["mean_ms"], 5), "gbps_median": round(gbps, 2),
+                          "frac_median": round(gbps / HBM_PEAK_GBPS, 4), "reps": steps}),
+              flush=True)
+        return
+    dec = bench_decode(b, steps, warmup, "decode_bf16", cold_reps=steps)
     S, msl = b.num_seqs, int(b.seq_lens.max())
     bps_ws = ops.pa_decode_workspace_size(S, 32, 8, 128, 16, msl)
     del b
@@ -539,8 +649,16 @@ def main():
         torch.cuda.empty_cache()
     if "long" not in skip:
         lb = W.long_bf16(device="cuda", poison=False)
-        extra["long_decode"] = bench_decode(lb, max(steps // 5, 5), max(warmup // 2, 2),
-                                            "long_bf16", cold_reps=20)
+        ld = bench_decode(lb, max(steps // 5, 5), max(warmup // 2, 2), "long_bf16",
+                          cold_reps=20)
+        ld["roofline"] = {"bound": "hbm", "kernel": "pa_decode_split_kernel + "
+                                                    "pa_decode_merge_kernel",
+                          "achieved": round(ld["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(ld["frac"], 4),
+                          "achieved_cold": round(ld["cold"]["gbps_median"], 1),
+                          "frac_cold": round(ld["cold"]["frac_median"], 4),
+                          "algorithmic_bytes": ld["kv_bytes"]}
+        extra["long_decode"] = ld
         del lb
         torch.cuda.empty_cache()
     if "beams" not in skip:
@@ -549,36 +667,46 @@ def main():
     if "swap" not in skip:
         extra["swap"] = bench_swap(5, 2)
         torch.cuda.empty_cache()
-    if args.sweep_block_size:
-        extra["block_size_sweep"] = sweep_block_size(max(steps // 2, 5), warmup)
+    if "indirection" not in skip:
+        extra["indirection"] = indirection_sweep(30)
 
+    cold = dec["cold"]
     result = {
         "metric": METRIC,
-        "value": round(dec["gbps"], 2),
+        "value": round(cold["gbps_median"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
         "prewarm_ms": PREWARM_MS,
-        "ms_per_step": round(dec["ms"], 5),
+        "ms_per_step": round(cold["median_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "timing": "value and ms_per_step: median over `steps` pa_decode calls, each after a "
+                  "clean flush of L2 and MALL and bracketed by its own HIP events; warm: "
+                  "back-to-back calls after the pre-warm",
         "config": {"workload": "decode_bf16: 64 sequences, lengths U[128,4096], 32 q / 8 kv "
                                "heads, head_dim 128, block_size 16, bf16 KV, fp32 accumulate",
                    "num_seqs": S, "kv_bytes_per_step": dec["kv_bytes"],
                    "workspace_bytes": bps_ws},
-        "decode_cold_caches": dec["cold"],
-        "roofline": {"bound": "hbm", "achieved": round(dec["gbps"], 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dec["gbps"] / HBM_PEAK_GBPS, 4),
+        "decode_cold_caches": cold,
+        "decode_warm": {"ms": round(dec["ms"], 5), "gbps": round(dec["gbps"], 2),
+                        "frac": round(dec["frac"], 4), "steps": steps},
+        "roofline": {"bound": "hbm", "achieved": round(cold["gbps_median"], 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(cold["frac_median"], 4),
+                     "frac_cold": round(cold["frac_median"], 4),
+                     "achieved_warm": round(dec["gbps"], 2),
+                     "frac_warm": round(dec["frac"], 4),
                      "traffic": measured_traffic(),
                      "algorithmic_bytes": dec["kv_bytes"],
                      "kernel": "pa_decode_split_kernel + pa_decode_merge_kernel (one pa_decode "
-                               "call; HIP events around the calls)",
+                               "call; HIP events around each call)",
                      "achievable_read_gbps": round(achievable, 1),
-                     "frac_of_achievable": round(dec["gbps"] / achievable, 4)},
+                     "frac_of_achievable": round(cold["gbps_median"] / achievable, 4)},
     }
     for k, v in extra.items():
         result[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -79,8 +79,9 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
  *   workspace    device scratch of at least pa_decode_workspace_size(...) bytes (may be NULL
  *                when that size is 0); contents need no initialisation
  *
- * Supported: head_dim in {64, 128, 256}; block_size in {8, 16, 32, 64} (16 is the pages'
- * default; the others serve the block-size trade-off); num_q_heads/num_kv_heads in
+ * Supported: head_dim in {64, 128, 256}; block_size in {1, 4, 8, 16, 32, 64} (16 is the
+ * pages' default; the others serve the block-size trade-off of cloudmash "Batching and
+ * PagedAttention", section "Choosing the block size"); num_q_heads/num_kv_heads in
  * {1, 2, 4, 8}; dtype F32 or BF16.  Pointers 16-byte aligned.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -95,6 +96,32 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * number of (sequence, kv head) work items, so the number of partials depends on it. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_seq_len);
+
+/*
+ * pa_decode_contiguous - the same decode over KV stored without paging: every (sequence, kv
+ * head) owns one contiguous slab of `capacity` token rows, as in a cache that reserves room for
+ * a maximum length up front.  It is pa_decode with the block-table lookup taken out (same split
+ * and merge, same unit of 16 tokens as 16-token blocks), the contiguous baseline that the
+ * pages weigh paging against: attention through a block table is slower than over one
+ * contiguous slab (cloudmash "Batching and PagedAttention", section "The indirection has a
+ * cost").  Result: as pa_decode on the same rows (up to fp32 summation order).
+ *
+ *   out, q       [num_seqs][num_q_heads][head_dim]
+ *   k, v         [num_seqs][num_kv_heads][capacity][head_dim]; row j < seq_lens[s] of
+ *                (s, kv head) is token j; rows past it are never used
+ *   seq_lens     [num_seqs] int32, 1 <= seq_lens[s] <= max_seq_len
+ *   capacity     token rows per (sequence, kv head): a multiple of 16, >= max_seq_len
+ *   workspace    pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, 16,
+ *                max_seq_len) bytes; contents need no initialisation
+ *
+ * Supported as pa_decode.  Errors as pa_decode, plus PA_ERR_INVALID_ARGUMENT for a capacity
+ * that is not a multiple of 16 or is below max_seq_len.
+ */
+pa_status pa_decode_contiguous(void* out, const void* q, const void* k, const void* v,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t capacity,
+                               int32_t max_seq_len, float scale, pa_dtype dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_decode_noalloc - for callers that cannot allocate device memory: code under HIP graph

@@ -156,6 +156,32 @@ def decode_ref(q, k_cache, v_cache, block_tables, seq_lens, scale: float, dtype:
     return out
 
 
+def decode_contiguous_ref(q, k, v, seq_lens, scale: float, dtype: str, seqs=None) -> np.ndarray:
+    """fp64 decode output [S, Hq, D] over KV kept without paging: k, v [S, Hkv, capacity, D],
+    row j < seq_lens[s] of (s, kv head) is token j.  This is the contiguous layout the pages
+    weigh paging against (cloudmash "Batching and PagedAttention", "The indirection has a
+    cost"); the attention is the same definition as decode_ref's, minus the table.
+    ``seqs`` restricts the work as in decode_ref."""
+    q = np.asarray(q)
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv != 0:
+        raise OracleInputError("num_q_heads must be a multiple of num_kv_heads")
+    sc = scale_f64(scale)
+    out = np.full((S, Hq, D), np.nan)
+    for s in selected(S, seqs):
+        L = int(seq_lens[s])
+        if L < 1 or L > k.shape[2]:
+            raise OracleInputError("seq_len outside [1, capacity]")
+        K = to_f64(k[s, :, :L, :], dtype)
+        V = to_f64(v[s, :, :L, :], dtype)
+        qs = to_f64(q[s], dtype)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            out[s, h] = attend(qs[h], K[g], V[g], sc)
+    return out
+
+
 # ------------------------------------------------------------------------------ prefill chunks
 def prefill_ref(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float,
                 dtype: str, block_size: int = 16, rows=None) -> np.ndarray:

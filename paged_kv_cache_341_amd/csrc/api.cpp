@@ -56,7 +56,16 @@ bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 constexpr int kSupportedBlock = 16;
 
 // Block sizes the decode kernels are built for (tokens per block).
-bool decode_block_supported(int b) { return b == 8 || b == 16 || b == 32 || b == 64; }
+bool decode_block_supported(int b) {
+  return b == 1 || b == 4 || b == 8 || b == 16 || b == 32 || b == 64;
+}
+
+// Tokens per unit of the decode split walk: the block size, or 16 for blocks smaller than 8
+// (their tokens are looked up one by one) and for contiguous KV (block_size 0 here).
+int decode_unit(int block_size) { return block_size >= 8 ? block_size : 16; }
+
+// Tokens per unit of the contiguous decode (the same walk as 16-token paged blocks).
+constexpr int kContiguousUnit = 16;
 
 // Blocks per decode split.  A split covers 256, 512 or 1024 tokens, the smallest that keeps
 // the number of workgroups near kTargetGroups when every sequence is max_seq_len long; the LDS
@@ -137,8 +146,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
       num_q_heads % num_kv_heads != 0)
     return 0;
   const int g = num_q_heads / num_kv_heads;
-  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, max_seq_len);
-  const int nblk = (max_seq_len + block_size - 1) / block_size;
+  const int unit = decode_unit(block_size);
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, unit, max_seq_len);
+  const int nblk = (max_seq_len + unit - 1) / unit;
   const int nsplit = (nblk + bps - 1) / bps;
   return decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
 }
@@ -168,14 +178,15 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d (supported: 64, 128, 256)", head_dim);
   if (!decode_block_supported(block_size))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d (supported: 8, 16, 32, 64)",
-                block_size);
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_decode: block_size %d (supported: 1, 4, 8, 16, 32, 64)", block_size);
   const int g = num_q_heads / num_kv_heads;
   if (!supported_group(g))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per kv head (supported: 1,2,4,8)",
                 g);
-  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, max_seq_len);
-  const int nblk = (max_seq_len + block_size - 1) / block_size;
+  const int unit = decode_unit(block_size);
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, unit, max_seq_len);
+  const int nblk = (max_seq_len + unit - 1) / unit;
   const int nsplit = (nblk + bps - 1) / bps;
   const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
   if (need > 0 && (!workspace || workspace_bytes < need))
@@ -220,6 +231,84 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   a.bf16 = dtype == PA_DTYPE_BF16;
   a.stream = static_cast<hipStream_t>(stream);
   return device_status(pa::launch_decode(a), "pa_decode launch");
+}
+
+pa_status pa_decode_contiguous(void* out, const void* q, const void* k, const void* v,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t capacity,
+                               int32_t max_seq_len, float scale, pa_dtype dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !q || !k || !v || !seq_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: null pointer argument");
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      capacity <= 0 || max_seq_len <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: sizes must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: num_q_heads %d not a multiple "
+                "of num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (!valid_dtype(dtype))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: unknown dtype");
+  if (capacity % kContiguousUnit != 0 || max_seq_len > capacity)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: capacity %d must be a multiple "
+                "of %d and at least max_seq_len %d", capacity, kContiguousUnit, max_seq_len);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: buffers must be 16-byte aligned");
+  if (!(scale > 0.f) || scale == __builtin_inff())
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: scale must be finite and "
+                "positive");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: head_dim %d (supported: 64, 128, "
+                "256)", head_dim);
+  const int g = num_q_heads / num_kv_heads;
+  if (!supported_group(g))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: %d query heads per kv head "
+                "(supported: 1,2,4,8)", g);
+  const int bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, kContiguousUnit, max_seq_len);
+  const int nunit = (max_seq_len + kContiguousUnit - 1) / kContiguousUnit;
+  const int nsplit = (nunit + bps - 1) / bps;
+  const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, nsplit);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_decode_contiguous: workspace %zu bytes, need "
+                "%zu", workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_contiguous: workspace must be 16-byte "
+                "aligned");
+  if (nsplit > 65535 || static_cast<int64_t>(num_seqs) * num_kv_heads > (int64_t{1} << 24))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_contiguous: grid too large");
+  PA_CHECK_CONTENTS("pa_decode_contiguous",
+                    pa::checked::tables(static_cast<hipStream_t>(stream), nullptr, seq_lens,
+                                        num_seqs, 0, 0, kContiguousUnit, max_seq_len));
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.block_tables = nullptr;
+  a.seq_lens = seq_lens;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * nsplit;
+  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             ((rows * 2 * sizeof(float) + 255) & ~size_t(255)))
+                  : nullptr;
+  a.contiguous = true;
+  a.capacity = capacity;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = kContiguousUnit;
+  a.max_blocks_per_seq = 0;
+  a.bps = bps;
+  a.nsplit_max = nsplit;
+  a.nsplit_tail = nsplit;
+  a.skip_blocks = nullptr;
+  a.slot_base = 0;
+  a.shared_split_keys = 1;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.bf16 = dtype == PA_DTYPE_BF16;
+  a.stream = static_cast<hipStream_t>(stream);
+  return device_status(pa::launch_decode(a), "pa_decode_contiguous launch");
 }
 
 // ------------------------------------------------------------------------- grouped decode

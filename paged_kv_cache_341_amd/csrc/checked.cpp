@@ -58,13 +58,14 @@ std::string tables(hipStream_t st, const int32_t* block_tables, const int32_t* s
                    int max_seq_len) {
   std::vector<int32_t> sl, bt;
   std::string err = fetch(st, seq_lens, static_cast<size_t>(num_seqs), sl);
-  if (err.empty())
+  if (err.empty() && block_tables)
     err = fetch(st, block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, bt);
   if (!err.empty()) return err;
   for (int s = 0; s < num_seqs; ++s) {
     const int L = sl[s];
     if (L < 1 || L > max_seq_len)
       return fmt("sequence %lld: seq_len %lld outside [1, max_seq_len %lld]", s, L, max_seq_len);
+    if (!block_tables) continue;
     const int used = (L + block_size - 1) / block_size;
     for (int j = 0; j < used; ++j) {
       const int32_t b = bt[static_cast<size_t>(s) * max_blocks_per_seq + j];

@@ -18,7 +18,8 @@ bool enabled();
 bool set_enabled(bool on);   // returns the previous setting
 
 // Each returns "" when the contents meet the preconditions, else a message naming the first
-// violation (a failed copy is reported the same way).
+// violation (a failed copy is reported the same way).  tables() with block_tables == nullptr
+// checks the lengths only.
 std::string tables(hipStream_t st, const int32_t* block_tables, const int32_t* seq_lens,
                    int num_seqs, int max_blocks_per_seq, int num_blocks, int block_size,
                    int max_seq_len);

@@ -33,6 +33,55 @@ struct DecodeShape {
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeThreads = kDecodeWaves * kWave;
 
+// Where the K (or V) rows of one (sequence, kv head) live.  The split item walks a sequence in
+// units of U consecutive tokens (unit u holds positions u*U .. u*U+U-1); `unit` gives the base
+// of unit u, uniform across the wave, and `row` the address of token k (0..U-1) of that unit.
+//
+// Paged, blocks of U tokens: unit u is physical block table[u] of the pool
+// [blocks][num_kv_heads][U][D], one wave-uniform (scalar) table read per unit.
+template <typename T, int D, int U>
+struct PagedRows {
+  const int32_t* table;        // this sequence's block table
+  int num_kv_heads, kvh;
+  __device__ __forceinline__ const T* unit(const T* cache, int u) const {
+    const int phys = wave_uniform(table[u]);
+    return cache + (static_cast<size_t>(phys) * num_kv_heads + kvh) * (static_cast<size_t>(U) * D);
+  }
+  __device__ __forceinline__ const T* row(const T*, const T* base, int, int k) const {
+    return base + static_cast<size_t>(k) * D;
+  }
+};
+
+// Paged, blocks of BT < U tokens (a unit spans U/BT blocks): every lane looks up the block of
+// the token it loads.  Tokens past the sequence end (the tail of its last unit) are read from
+// its last token instead, so no table entry past ceil(len/BT) is touched; they are masked out
+// by selection afterwards like every other tail slot.
+template <typename T, int D, int U, int BT>
+struct PagedSmallRows {
+  static_assert(BT < U && U % BT == 0, "small blocks must tile a unit");
+  const int32_t* table;
+  int num_kv_heads, kvh, len;
+  __device__ __forceinline__ const T* unit(const T* cache, int) const { return cache; }
+  __device__ __forceinline__ const T* row(const T* cache, const T*, int u, int k) const {
+    const int tok = min(u * U + k, len - 1);
+    const int phys = table[tok / BT];
+    return cache + ((static_cast<size_t>(phys) * num_kv_heads + kvh) * BT + tok % BT) * D;
+  }
+};
+
+// Contiguous, no table: the cache is [num_seqs][num_kv_heads][capacity][D] with capacity a
+// multiple of U, so every unit of a sequence lies inside its own slab.
+template <typename T, int D, int U>
+struct ContiguousRows {
+  size_t slab;                 // element offset of (sequence, kv head, token 0)
+  __device__ __forceinline__ const T* unit(const T* cache, int u) const {
+    return cache + slab + static_cast<size_t>(u) * U * D;
+  }
+  __device__ __forceinline__ const T* row(const T*, const T* base, int, int k) const {
+    return base + static_cast<size_t>(k) * D;
+  }
+};
+
 // Partial dot product of one 16-byte chunk of q with one chunk of K.
 __device__ __forceinline__ float chunk_dot(uint4 q, uint4 k, float acc, bf16_t) {
   acc = dot2_bf16(q.x, k.x, acc);
@@ -70,14 +119,14 @@ __device__ __forceinline__ void store_out(bf16_t* p, float v) {
 // `Batch` blocks per wave are loaded together before their math (0: 64 tokens' worth).
 // With `Prio`, the K phase runs at wave priority 2 and the V phase at 0, each one band higher
 // when `late` (a split dispatched late): splits that have made less progress issue first.
-template <typename T, int D, int G, int B, int Waves, int Batch = 0, bool Prio = false>
+template <typename T, int D, int G, int B, int Waves, int Batch = 0, bool Prio = false,
+          typename Rows>
 __device__ __forceinline__ void decode_split_item(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ skip_blocks, int slot_base, int num_kv_heads,
-    int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2, int s, int kvh,
-    int split, float* smem, float (*red)[G], float* stat_m, float* stat_l, bool late = false) {
+    const Rows& rows, int L, const int32_t* __restrict__ skip_blocks, int slot_base,
+    int num_kv_heads, int bps, int nsplit_max, float scale_log2, int s, int kvh, int split,
+    float* smem, float (*red)[G], float* stat_m, float* stat_l, bool late = false) {
   using S = DecodeShape<T, D, G, B>;
   constexpr int kBlock = B;
   constexpr int kDecodeBatch = Batch > 0 ? Batch : S::kBatch;
@@ -87,7 +136,6 @@ __device__ __forceinline__ void decode_split_item(
   const T tag{};
   float* logits = smem;                                  // [bps*16][G]
 
-  const int L = seq_lens[s];
   const int nblk = (L + kBlock - 1) / kBlock;
   // leading blocks another kernel covers (a prefix shared with the sequence's group)
   const int skip = skip_blocks ? min(max(skip_blocks[s], 0), L / kBlock) : 0;
@@ -100,8 +148,6 @@ __device__ __forceinline__ void decode_split_item(
   const int wave = wave_uniform(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int Hq = num_kv_heads * G;
-  const int32_t* table = block_tables + static_cast<size_t>(s) * max_blocks_per_seq;
-  const size_t slab = static_cast<size_t>(kBlock) * D;   // elements per (block, kv head)
 
   if constexpr (Prio) {
     if (late) __builtin_amdgcn_s_setprio(3);
@@ -125,14 +171,14 @@ __device__ __forceinline__ void decode_split_item(
       for (int j = 0; j < kDecodeBatch; ++j) {
         const int lb = i0 + j * Waves;
         if (lb < b_end) {
-          const int phys = wave_uniform(table[lb]);
-          const T* kb = k_cache + (static_cast<size_t>(phys) * num_kv_heads + kvh) * slab;
+          const T* kb = rows.unit(k_cache, lb);
 #pragma unroll
-          for (int k = 0; k < S::kTpb1; ++k)
+          for (int k = 0; k < S::kTpb1; ++k) {
+            const T* kt = rows.row(k_cache, kb, lb, k * S::kGr1 + grp);
 #pragma unroll
             for (int r = 0; r < S::kR1; ++r)
-              kr[j][k][r] = load16_stream(
-                  kb + ((k * S::kGr1 + grp) * kCpr + sub + r * S::kW1) * kEpc);
+              kr[j][k][r] = load16_stream(kt + (sub + r * S::kW1) * kEpc);
+          }
         }
       }
 #pragma unroll
@@ -211,14 +257,14 @@ __device__ __forceinline__ void decode_split_item(
     for (int j = 0; j < kDecodeBatch; ++j) {
       const int lb = i0 + j * Waves;
       if (lb < b_end) {
-        const int phys = wave_uniform(table[lb]);
-        const T* vb = v_cache + (static_cast<size_t>(phys) * num_kv_heads + kvh) * slab;
+        const T* vb = rows.unit(v_cache, lb);
 #pragma unroll
-        for (int k = 0; k < S::kTpb3; ++k)
+        for (int k = 0; k < S::kTpb3; ++k) {
+          const T* vt = rows.row(v_cache, vb, lb, k * S::kGr3 + grp);
 #pragma unroll
           for (int r = 0; r < S::kR3; ++r)
-            vr[j][k][r] =
-                load16_stream(vb + ((k * S::kGr3 + grp) * kCpr + sub + r * S::kW3) * kEpc);
+            vr[j][k][r] = load16_stream(vt + (sub + r * S::kW3) * kEpc);
+        }
       }
     }
 #pragma unroll

@@ -23,6 +23,12 @@ struct DecodeArgs {
   const int32_t* skip_blocks;
   int slot_base, shared_split_keys;
   int nsplit_tail;     // grid.y of the split kernel
+  // Contiguous KV ([num_seqs][num_kv_heads][capacity][head_dim], no table) instead of a pool.
+  bool contiguous;
+  int capacity;
+  // block_size: tokens per pool block.  The split walk goes in units of block_size tokens, or of
+  // 16 tokens when blocks are smaller than 8 (each token's block is then looked up on its own)
+  // and for contiguous KV; bps counts units.
   int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
   int bps, nsplit_max;
   float scale_log2;

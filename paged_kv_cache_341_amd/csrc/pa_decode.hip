@@ -29,13 +29,16 @@
 
 namespace pa {
 
-template <typename T, int D, int G, int B>
+// U: tokens per unit of the split walk (the pool's block size when BT == U); BT: tokens per
+// pool block (BT < U: blocks smaller than a unit, looked up per token); Contig: no table, the
+// cache is [num_seqs][num_kv_heads][capacity][D].
+template <typename T, int D, int G, int U, int BT, bool Contig>
 __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ skip_blocks, int slot_base, int num_kv_heads,
-    int max_blocks_per_seq, int bps, int nsplit_max, float scale_log2) {
+    int max_blocks_per_seq, int capacity, int bps, int nsplit_max, float scale_log2) {
   extern __shared__ float smem[];
   __shared__ float red[kDecodeWaves][G];
   __shared__ float stat_m[G];
@@ -47,11 +50,32 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   // through the same XCD's L2.
   // The splits dispatched last are the second half of the split-index range (grid.y): they
   // take the higher of the two priority bands (see decode_split_item).
-  decode_split_item<T, D, G, B, kDecodeWaves, 0, true>(
-      out, ws_ml, ws_acc, q, k_cache, v_cache, block_tables, seq_lens, skip_blocks, slot_base,
-      num_kv_heads, max_blocks_per_seq, bps, nsplit_max, scale_log2,
-      static_cast<int>(blockIdx.x) / num_kv_heads, static_cast<int>(blockIdx.x) % num_kv_heads,
-      static_cast<int>(blockIdx.y), smem, red, stat_m, stat_l, blockIdx.y * 2 >= gridDim.y);
+  const int s = static_cast<int>(blockIdx.x) / num_kv_heads;
+  const int kvh = static_cast<int>(blockIdx.x) % num_kv_heads;
+  const int L = seq_lens[s];
+  const bool late = blockIdx.y * 2 >= gridDim.y;
+  if constexpr (Contig) {
+    const ContiguousRows<T, D, U> rows{(static_cast<size_t>(s) * num_kv_heads + kvh) *
+                                       static_cast<size_t>(capacity) * D};
+    decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
+        out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
+        bps, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        stat_l, late);
+  } else if constexpr (BT == U) {
+    const PagedRows<T, D, U> rows{block_tables + static_cast<size_t>(s) * max_blocks_per_seq,
+                                  num_kv_heads, kvh};
+    decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
+        out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
+        bps, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        stat_l, late);
+  } else {
+    const PagedSmallRows<T, D, U, BT> rows{
+        block_tables + static_cast<size_t>(s) * max_blocks_per_seq, num_kv_heads, kvh, L};
+    decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
+        out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
+        bps, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        stat_l, late);
+  }
 }
 
 // Combine the splits of one (sequence, query head) row; one wave per row.  Lanes first read
@@ -194,20 +218,20 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   for (int e = 0; e < kPer; ++e) store_out(out + static_cast<size_t>(row) * D + lane + e * kWave, num[e] * inv);
 }
 
-template <typename T, int D, int G, int B>
+template <typename T, int D, int G, int U, int BT, bool Contig>
 hipError_t launch_decode_tb(const DecodeArgs& a) {
-  const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * B * G,
+  const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * U * G,
                                       static_cast<size_t>(kDecodeWaves) * G * D) * sizeof(float);
   const dim3 grid_split(a.num_seqs * a.num_kv_heads, a.nsplit_tail);
-  hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G, B>), grid_split, dim3(kDecodeThreads),
-                     lds, a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache),
+  hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G, U, BT, Contig>), grid_split,
+                     dim3(kDecodeThreads), lds, a.stream, static_cast<T*>(a.out), a.ws_ml,
+                     a.ws_acc, static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_tables, a.seq_lens,
-                     a.skip_blocks, a.slot_base, a.num_kv_heads, a.max_blocks_per_seq, a.bps,
-                     a.nsplit_max, a.scale_log2);
+                     a.skip_blocks, a.slot_base, a.num_kv_heads, a.max_blocks_per_seq,
+                     a.capacity, a.bps, a.nsplit_max, a.scale_log2);
   if (a.nsplit_max > 1) {
     const int rows = a.num_seqs * a.num_kv_heads * G;
-    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D, B>),
+    hipLaunchKernelGGL((pa_decode_merge_kernel<T, D, U>),
                        dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
                        a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens,
                        a.skip_blocks, a.slot_base, a.shared_split_keys, rows,
@@ -230,11 +254,14 @@ hipError_t launch_decode_merge(const DecodeArgs& a) {
 
 template <typename T, int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a) {
+  if (a.contiguous) return launch_decode_tb<T, D, G, 16, 16, true>(a);
   switch (a.block_size) {
-    case 8: return launch_decode_tb<T, D, G, 8>(a);
-    case 16: return launch_decode_tb<T, D, G, 16>(a);
-    case 32: return launch_decode_tb<T, D, G, 32>(a);
-    case 64: return launch_decode_tb<T, D, G, 64>(a);
+    case 1: return launch_decode_tb<T, D, G, 16, 1, false>(a);
+    case 4: return launch_decode_tb<T, D, G, 16, 4, false>(a);
+    case 8: return launch_decode_tb<T, D, G, 8, 8, false>(a);
+    case 16: return launch_decode_tb<T, D, G, 16, 16, false>(a);
+    case 32: return launch_decode_tb<T, D, G, 32, 32, false>(a);
+    case 64: return launch_decode_tb<T, D, G, 64, 64, false>(a);
   }
   return hipErrorInvalidValue;
 }

@@ -139,9 +139,11 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
       }
       const int s = wave_uniform(lo);
       const int split = j - (s > 0 ? dscan[s - 1] : 0);
+      const PagedRows<bf16_t, kD, kBlock> rows{
+          dec_tables + static_cast<size_t>(s) * dec_max_blocks, num_kv_heads, kvh};
       decode_split_item<bf16_t, kD, G, kBlock, kWaves, kMixedDecodeBatch>(
-          dec_out, ws_ml, ws_acc, dec_q, k_cache, v_cache, dec_tables, dec_seq_lens, nullptr, 0,
-          num_kv_heads, dec_max_blocks, bps, nsplit_max, scale_log2, s, kvh, split,
+          dec_out, ws_ml, ws_acc, dec_q, k_cache, v_cache, rows, dec_seq_lens[s], nullptr, 0,
+          num_kv_heads, bps, nsplit_max, scale_log2, s, kvh, split,
           reinterpret_cast<float*>(ring), dred, dstat_m, dstat_l);
     }
     __syncthreads();                               // the ring is reused by the next item

@@ -23,7 +23,8 @@ PA_DTYPE_BF16 = 1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID_ARGUMENT", 2: "PA_ERR_UNSUPPORTED",
                 3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_DEVICE"}
 
-EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_noalloc", "pa_decode_grouped",
+EXPORTED = ("pa_decode", "pa_decode_workspace_size", "pa_decode_contiguous", "pa_decode_noalloc",
+            "pa_decode_grouped",
             "pa_decode_grouped_workspace_size", "pa_mixed_step", "pa_mixed_workspace_size",
             "pa_prefill_chunk",
             "pa_prefill_workspace_size", "kv_append", "cow_copy_blocks", "pa_status_string",
@@ -83,6 +84,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               _i32, _i32, _f32, ctypes.c_int, _vp, _sz, _vp]
     lib.pa_decode_workspace_size.restype = _sz
     lib.pa_decode_workspace_size.argtypes = [_i32] * 6
+    lib.pa_decode_contiguous.restype = ctypes.c_int
+    lib.pa_decode_contiguous.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _f32, ctypes.c_int, _vp, _sz, _vp]
     lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _f32, ctypes.c_int, _vp]
@@ -187,6 +191,30 @@ def pa_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                        _ptr(seq_lens), S, Hq, Hkv, D, B, NB, block_tables.shape[1],
                        int(max_seq_len), float(scale), _dtype_code(q), _ptr(workspace),
                        ws_bytes, _stream(q, stream))
+    _check(st)
+    return out
+
+
+def pa_decode_contiguous(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode over contiguous KV: k, v [num_seqs, num_kv_heads, capacity, head_dim], row j of
+    (s, kv head) is token j (see pagedattn.h)."""
+    lib = load_library()
+    _contig(out, q, k, v, seq_lens)
+    _need(seq_lens.dtype == torch.int32, "seq_lens must be int32")
+    S, Hq, D = q.shape
+    S2, Hkv, cap, D2 = k.shape
+    _need(S2 == S and D2 == D and tuple(v.shape) == tuple(k.shape), "k/v shape mismatch")
+    _need(tuple(out.shape) == tuple(q.shape), "out must match q")
+    _need(out.dtype == q.dtype == k.dtype == v.dtype, "dtypes must match")
+    ws_need = pa_decode_workspace_size(S, Hq, Hkv, D, 16, max_seq_len)
+    if workspace is None and ws_need:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_contiguous(_ptr(out), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens), S, Hq,
+                                  Hkv, D, cap, int(max_seq_len), float(scale), _dtype_code(q),
+                                  _ptr(workspace), ws_bytes, _stream(q, stream))
     _check(st)
     return out
 

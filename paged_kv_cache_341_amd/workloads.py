@@ -84,6 +84,35 @@ class DecodeBatch:
 
 
 @dataclass
+class ContiguousDecode:
+    """Inputs of one decode over KV kept without paging: k, v [S, Hkv, capacity, D], row j of
+    (s, kv head) holds token j."""
+
+    q: torch.Tensor                 # [S, Hq, D]
+    k: torch.Tensor                 # [S, Hkv, capacity, D]
+    v: torch.Tensor
+    seq_lens: np.ndarray            # int32 [S]
+    scale: float
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    name: str = ""
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max())
+
+    @property
+    def capacity(self) -> int:
+        return int(self.k.shape[2])
+
+
+@dataclass
 class MixedStep:
     """One continuous-batching iteration: append, then prefill chunks and decodes."""
 
@@ -192,6 +221,28 @@ def make_decode(seq_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, he
                        block_size=block_size, dtype=dtype, name=name)
 
 
+def make_contiguous_decode(seq_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, dtype: str, seed: int, *, capacity: Optional[int] = None,
+                           poison: bool = True, device="cpu", name: str = "") -> ContiguousDecode:
+    """A decode batch with contiguous KV: q, then K and V drawn directly in the
+    [S, Hkv, capacity, D] layout (capacity: the longest length rounded up to 16 unless given).
+    Rows past a sequence's length are NaN when ``poison`` is on."""
+    lens = np.asarray([int(x) for x in seq_lens], dtype=np.int32)
+    cap = int(capacity) if capacity is not None else int(-(-int(lens.max()) // 16) * 16)
+    gen = _gen(seed, device)
+    S = len(lens)
+    q = _randn((S, num_q_heads, head_dim), gen, dtype, device)
+    k = _randn((S, num_kv_heads, cap, head_dim), gen, dtype, device)
+    v = _randn((S, num_kv_heads, cap, head_dim), gen, dtype, device)
+    if poison:
+        past = torch.from_numpy(np.arange(cap)[None, :] >= lens[:, None]).to(device)
+        k.masked_fill_(past[:, None, :, None], float("nan"))
+        v.masked_fill_(past[:, None, :, None], float("nan"))
+    return ContiguousDecode(q=q, k=k, v=v, seq_lens=lens, scale=default_scale(head_dim),
+                            num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                            head_dim=head_dim, dtype=dtype, name=name)
+
+
 def make_grouped_decode(groups: Sequence[tuple], num_q_heads: int, num_kv_heads: int,
                         head_dim: int, seed: int, *, dtype: str = "bf16", poison: bool = True,
                         device="cpu") -> DecodeBatch:
@@ -254,6 +305,21 @@ def decode_bf16(device="cpu", poison: bool = True, seed: int = SEED_BASE + 2,
     lens = rng.integers(lo, hi + 1, size=num_seqs)
     return make_decode(lens, 32, 8, 128, "bf16", seed, rng=rng, poison=poison, device=device,
                        name="decode_bf16", block_size=block_size, scatter=scatter)
+
+
+def decode_bf16_contiguous(device="cpu", poison: bool = True,
+                           seed: int = SEED_BASE + 2) -> ContiguousDecode:
+    """Workload 2's lengths (the same draw) and heads, with contiguous KV of capacity 4096."""
+    lens = np.random.default_rng(seed).integers(128, 4097, size=64)
+    return make_contiguous_decode(lens, 32, 8, 128, "bf16", seed, capacity=4096, poison=poison,
+                                  device=device, name="decode_bf16_contiguous")
+
+
+def long_bf16_contiguous(device="cpu", poison: bool = True,
+                         seed: int = SEED_BASE + 3) -> ContiguousDecode:
+    """Workload 3's shape (32 x 32768 tokens, 16/4 heads, head_dim 256) with contiguous KV."""
+    return make_contiguous_decode([32768] * 32, 16, 4, 256, "bf16", seed, poison=poison,
+                                  device=device, name="long_bf16_contiguous")
 
 
 def long_bf16(device="cpu", poison: bool = True, seed: int = SEED_BASE + 3,

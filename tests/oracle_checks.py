@@ -388,9 +388,31 @@ def check_subsets(ref):
         assert np.all(np.isnan(part[rest])), rows
 
 
+def check_contiguous(ref):
+    """The contiguous-KV decode equals loop brute force on the logical rows (S1 for the
+    unpaged layout), ignores rows past each length (NaN there), and equals the paged oracle on
+    the same rows scattered through a table."""
+    t = Tiny([1, 7, 33, 16], Hq=4, Hkv=2, D=8, block_size=4, seed=161)
+    cap = 48
+    k = np.full((4, 2, cap, 8), np.nan, np.float32)
+    v = np.full((4, 2, cap, 8), np.nan, np.float32)
+    for s, L in enumerate(t.lengths):
+        k[s, :, :L] = t.K[s].transpose(1, 0, 2)
+        v[s, :, :L] = t.V[s].transpose(1, 0, 2)
+    lens = np.asarray(t.lengths, np.int32)
+    out = ref.decode_contiguous_ref(t.q, k, v, lens, t.scale, "f32")
+    for s, L in enumerate(t.lengths):
+        for h in range(4):
+            g = h // 2
+            want = brute.attention_row(t.q[s, h].tolist(), t.K[s][:, g].tolist(),
+                                       t.V[s][:, g].tolist(), t.scale, L)
+            assert np.max(np.abs(out[s, h] - want)) <= 1e-12, (s, h)
+    assert np.max(np.abs(out - t.decode(ref))) <= 1e-13
+
+
 ALL_CHECKS = [check_hand_example, check_brute_force, check_permutation,
               check_block_size_invariance, check_row_sums, check_single_token, check_zero_query,
               check_constant_values, check_needle, check_sdpa, check_chunk_positions,
               check_append_roundtrip, check_cow, check_swap, check_nan_poison,
               check_bf16_widening,
-              check_bf16_decode, check_subsets]
+              check_bf16_decode, check_subsets, check_contiguous]

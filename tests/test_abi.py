@@ -54,12 +54,33 @@ def _decode(**kw):
     (dict(q=None), INV), (dict(S=0), INV), (dict(Hq=6, Hkv=4), INV), (dict(maxlen=129), INV),
     (dict(out=P + 2), INV), (dict(dtype=7), INV), (dict(scale=float("nan")), INV),
     (dict(scale=0.0), INV), (dict(scale=-0.1), INV), (dict(scale=float("inf")), INV),
-    (dict(D=96), UNS), (dict(B=4, MB=32), UNS), (dict(B=128, MB=1), UNS), (dict(Hq=32, Hkv=2), UNS),
+    (dict(D=96), UNS), (dict(B=2, MB=64), UNS), (dict(B=128, MB=1), UNS), (dict(Hq=32, Hkv=2), UNS),
     (dict(maxlen=128 * 16, MB=128, S=64, wsb=16), WS),
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
     assert ops.load_library().pa_last_error().decode().startswith("pa_decode")
+
+
+def _contiguous(**kw):
+    a = dict(out=P, q=P, k=P, v=P, sl=P, S=4, Hq=8, Hkv=2, D=128, cap=128, maxlen=100,
+             scale=0.1, dtype=1, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    lib = ops.load_library()
+    return lib.pa_decode_contiguous(a["out"], a["q"], a["k"], a["v"], a["sl"], a["S"], a["Hq"],
+                                    a["Hkv"], a["D"], a["cap"], a["maxlen"], a["scale"],
+                                    a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), INV), (dict(S=0), INV), (dict(Hq=6, Hkv=4), INV), (dict(cap=120), INV),
+    (dict(maxlen=129), INV), (dict(v=P + 4), INV), (dict(scale=0.0), INV), (dict(dtype=3), INV),
+    (dict(D=96), UNS), (dict(Hq=32, Hkv=2), UNS),
+    (dict(S=64, cap=4096, maxlen=4096, wsb=16), WS),
+])
+def test_decode_contiguous_rejects(kw, status):
+    assert _contiguous(**kw) == status
+    assert ops.load_library().pa_last_error().decode().startswith("pa_decode_contiguous")
 
 
 def test_decode_noalloc_refuses_sizes_beyond_its_scratch():

@@ -70,11 +70,11 @@ def test_decode_f32_ragged(G, D):
     assert_close(widen(out), oracle_decode(b), F32_ATOL, F32_RTOL, f"f32 G{G} D{D}")
 
 
-@pytest.mark.parametrize("B", [8, 32, 64])
+@pytest.mark.parametrize("B", [1, 4, 8, 32, 64])
 def test_decode_other_block_sizes(B):
-    """Block sizes 8, 32 and 64 (16 is the default everywhere else): ragged lengths around
-    block edges, NaN in every unfilled slot, G = 4, and an fp32 case."""
-    lens = [1, B - 1, B, B + 1, 3 * B + 5, 700, 2047, 4100]
+    """Block sizes 1, 4, 8, 32 and 64 (16 is the default everywhere else): ragged lengths
+    around block edges, NaN in every unfilled slot, G = 4, and an fp32 case."""
+    lens = sorted(set(max(1, x) for x in [1, B - 1, B, B + 1, 3 * B + 5, 700, 2047, 4100]))
     say(f"case: bf16 decode, block size {B}")
     b = W.make_decode(lens, 16, 4, 128, "bf16", seed=1600 + B, device=DEV, block_size=B)
     out = run_decode(b)
@@ -127,6 +127,79 @@ def test_decode_needle(jstar):
     assert_close(widen(out), want, ATOL, RTOL, "needle")
     target = b.v_cache[phys, 0, jstar % 16].float().cpu().numpy()
     assert np.max(np.abs(widen(out)[0, 0] - target)) < 0.05
+
+
+@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("jstar", [0, 3, 4, 15, 16, 2999])
+def test_decode_small_block_needle(B, jstar):
+    """Needles at block and 16-token unit edges with blocks smaller than a unit (each token's
+    block is looked up on its own)."""
+    L = 3000
+    say(f"case: needle at {jstar} of {L}, block size {B}")
+    b = W.make_decode([L, 77], 4, 1, 128, "bf16", seed=710 + B, device=DEV, block_size=B)
+    phys = int(b.block_tables[0, jstar // B])
+    qv = b.q[0, 0].float()
+    b.k_cache[phys, 0, jstar % B] = (qv * (40.0 / (b.scale * float(qv @ qv)))).to(torch.bfloat16)
+    out = run_decode(b)
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, "small-block needle")
+    target = b.v_cache[phys, 0, jstar % B].float().cpu().numpy()
+    assert np.max(np.abs(widen(out)[0, 0] - target)) < 0.05
+
+
+# ------------------------------------------------------------------------------ contiguous KV
+def run_contiguous(c):
+    """pa_decode_contiguous with output and workspace between canary guard regions."""
+    from tests.gpu_util import Guarded, guarded_like
+    g = guarded_like(c.q)
+    out = g.tensor(c.q.shape, c.q.dtype)
+    n = ops.pa_decode_workspace_size(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, 16,
+                                     c.max_seq_len)
+    gw = Guarded(n, device=DEV) if n else None
+    ops.pa_decode_contiguous(out, c.q, c.k, c.v, dev_i32(c.seq_lens), c.max_seq_len, c.scale,
+                             workspace=None if gw is None else gw.bytes())
+    g.check("contiguous out")
+    if gw is not None:
+        gw.check("contiguous workspace")
+    return out
+
+
+def oracle_contiguous(c, seqs=None):
+    return ref.decode_contiguous_ref(raw(c.q), raw(c.k), raw(c.v), c.seq_lens, c.scale, c.dtype,
+                                     seqs=seqs)
+
+
+@pytest.mark.parametrize("G,D,dtype", [(1, 64, "bf16"), (4, 128, "bf16"), (8, 128, "bf16"),
+                                       (4, 256, "bf16"), (2, 128, "f32"), (8, 256, "f32")])
+def test_decode_contiguous_ragged(G, D, dtype):
+    """KV without paging (one slab per sequence and kv head): ragged lengths, NaN in every row
+    past a length, bf16 and fp32; length-1 rows return their V row exactly."""
+    say(f"case: contiguous decode G={G} D={D} {dtype}")
+    lens = [1, 2, 15, 16, 17, 100, 513, 1000, 2049]
+    c = W.make_contiguous_decode(lens, 2 * G, 2, D, dtype, seed=1800 + G + D, device=DEV,
+                                 capacity=2064)
+    out = run_contiguous(c)
+    atol, rtol = (ATOL, RTOL) if dtype == "bf16" else (F32_ATOL, F32_RTOL)
+    assert_close(widen(out), oracle_contiguous(c), atol, rtol, f"contiguous G{G} D{D} {dtype}")
+    for h in range(2 * G):
+        assert torch.equal(out[0, h], c.v[0, h // G, 0])
+
+
+def test_decode_contiguous_full_size():
+    """The 64-sequence batch's lengths and heads (capacity 4096) and the 32 x 32768 long
+    context (16/4 heads, D256) in the contiguous layout, every sequence against the oracle."""
+    say("case: contiguous decode at full size (64 x U[128,4096]; 32 x 32768 D256)")
+    c = W.decode_bf16_contiguous(device=DEV)
+    assert_close(widen(run_contiguous(c)), oracle_contiguous(c), ATOL, RTOL,
+                 "decode_bf16 contiguous")
+    del c
+    torch.cuda.empty_cache()
+    c = W.long_bf16_contiguous(device=DEV)
+    got = widen(run_contiguous(c))
+    for first in range(0, 32, 8):
+        rows = list(range(first, first + 8))
+        want = ref.decode_contiguous_ref(raw(c.q[rows]), raw(c.k[rows]), raw(c.v[rows]),
+                                         c.seq_lens[rows], c.scale, "bf16")
+        assert_close(got[rows], want, ATOL, RTOL, f"long contiguous {first}-{first + 7}")
 
 
 def test_decode_permutation_invariant_and_deterministic():

@@ -12,6 +12,15 @@ _orig_cow = paged_ref.cow_ref
 _orig_swap = paged_ref.swap_ref
 _orig_gather = paged_ref.gather_tokens
 _orig_selected = paged_ref.selected
+_orig_contig = paged_ref.decode_contiguous_ref
+
+
+def _contig_one_row_too_many(q, k, v, seq_lens, scale, dtype, seqs=None):
+    return _orig_contig(q, k, v, np.asarray(seq_lens) + 1, scale, dtype, seqs)
+
+
+def _contig_heads_swapped(q, k, v, seq_lens, scale, dtype, seqs=None):
+    return _orig_contig(q, k[:, ::-1], v[:, ::-1], seq_lens, scale, dtype, seqs)
 
 
 def _gather_ignoring_table(cache, table_row, length, block_size):
@@ -33,6 +42,8 @@ MUTATIONS = {
                               _orig_selected(n, w, first + 1)),
     "subset_drops_last": ("selected", lambda n, w=None, first=0: _orig_selected(n, w, first)[:-1]),
     "subset_ignored": ("selected", lambda n, w=None, first=0: _orig_selected(n, None, first)),
+    "contiguous_row_past_length": ("decode_contiguous_ref", _contig_one_row_too_many),
+    "contiguous_kv_heads_swapped": ("decode_contiguous_ref", _contig_heads_swapped),
     "softmax_unnormalised": ("softmax_weights",
                              lambda x: np.exp(x - np.max(x, axis=-1, keepdims=True))),
     "softmax_sign_flipped": ("softmax_weights", lambda x: _orig_softmax(-x)),
