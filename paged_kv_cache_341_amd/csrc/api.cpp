@@ -67,6 +67,8 @@ int decode_unit(int block_size) { return block_size >= 8 ? block_size : 16; }
 // Tokens per unit of the contiguous decode (the same walk as 16-token paged blocks).
 constexpr int kContiguousUnit = 16;
 
+constexpr int kMaxSplitBlocks = 256;
+
 // Blocks per decode split.  A split covers 256, 512 or 1024 tokens, the smallest that keeps
 // the number of workgroups near kTargetGroups when every sequence is max_seq_len long; the LDS
 // score buffer caps a split at 8192/G tokens.  PA_DECODE_SPLIT_BLOCKS overrides the block
@@ -91,6 +93,9 @@ int plan_blocks_per_split(int num_seqs, int num_kv_heads, int group, int block_s
     bps = std::max(1, tokens / block_size);
   }
   bps = std::min(bps, cap);
+  // a wave of a split keeps its table entries one per lane: at most 64 per wave, and the split
+  // kernels run at least 4 waves per split
+  bps = std::min(bps, kMaxSplitBlocks);
   bps = std::max(bps, 1);
   return std::min(bps, std::max(nblk, 1));
 }

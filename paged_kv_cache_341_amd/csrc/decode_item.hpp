@@ -37,14 +37,28 @@ constexpr int kDecodeThreads = kDecodeWaves * kWave;
 // units of U consecutive tokens (unit u holds positions u*U .. u*U+U-1); `unit` gives the base
 // of unit u, uniform across the wave, and `row` the address of token k (0..U-1) of that unit.
 //
+// Every row policy has prepare(first, count, stride): the calling wave will visit units
+// first, first + stride, ... (count of them, count <= 64), and may fetch what it needs for them
+// up front.
+//
 // Paged, blocks of U tokens: unit u is physical block table[u] of the pool
-// [blocks][num_kv_heads][U][D], one wave-uniform (scalar) table read per unit.
+// [blocks][num_kv_heads][U][D].  prepare() reads the wave's table entries once, one per lane
+// (in the same round trip as the query rows), and unit() picks them with readlane, so no load
+// batch waits on a table read.
 template <typename T, int D, int U>
 struct PagedRows {
   const int32_t* table;        // this sequence's block table
   int num_kv_heads, kvh;
+  int first = 0, stride = 1;
+  int ids = 0;                 // lane l: table[first + l * stride] (lanes < count)
+  __device__ __forceinline__ void prepare(int first_unit, int count, int stride_units) {
+    first = first_unit;
+    stride = stride_units;
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    ids = lane < count ? table[first + lane * stride] : 0;
+  }
   __device__ __forceinline__ const T* unit(const T* cache, int u) const {
-    const int phys = wave_uniform(table[u]);
+    const int phys = __builtin_amdgcn_readlane(ids, wave_uniform((u - first) / stride));
     return cache + (static_cast<size_t>(phys) * num_kv_heads + kvh) * (static_cast<size_t>(U) * D);
   }
   __device__ __forceinline__ const T* row(const T*, const T* base, int, int k) const {
@@ -61,6 +75,7 @@ struct PagedSmallRows {
   static_assert(BT < U && U % BT == 0, "small blocks must tile a unit");
   const int32_t* table;
   int num_kv_heads, kvh, len;
+  __device__ __forceinline__ void prepare(int, int, int) {}
   __device__ __forceinline__ const T* unit(const T* cache, int) const { return cache; }
   __device__ __forceinline__ const T* row(const T* cache, const T*, int u, int k) const {
     const int tok = min(u * U + k, len - 1);
@@ -74,6 +89,7 @@ struct PagedSmallRows {
 template <typename T, int D, int U>
 struct ContiguousRows {
   size_t slab;                 // element offset of (sequence, kv head, token 0)
+  __device__ __forceinline__ void prepare(int, int, int) {}
   __device__ __forceinline__ const T* unit(const T* cache, int u) const {
     return cache + slab + static_cast<size_t>(u) * U * D;
   }
@@ -124,7 +140,7 @@ template <typename T, int D, int G, int B, int Waves, int Batch = 0, bool Prio =
 __device__ __forceinline__ void decode_split_item(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
-    const Rows& rows, int L, const int32_t* __restrict__ skip_blocks, int slot_base,
+    Rows rows, int L, const int32_t* __restrict__ skip_blocks, int slot_base,
     int num_kv_heads, int bps, int nsplit_max, float scale_log2, int s, int kvh, int split,
     float* smem, float (*red)[G], float* stat_m, float* stat_l, bool late = false) {
   using S = DecodeShape<T, D, G, B>;
@@ -153,6 +169,9 @@ __device__ __forceinline__ void decode_split_item(
     if (late) __builtin_amdgcn_s_setprio(3);
     else __builtin_amdgcn_s_setprio(2);
   }
+
+  // this wave's units of the split: b_begin + wave, + Waves, ... below b_end
+  rows.prepare(b_begin + wave, max(0, (b_end - b_begin - wave + Waves - 1) / Waves), Waves);
 
   // ---------------------------------------------------------------- phase 1: scores
   {
