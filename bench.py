@@ -37,15 +37,16 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 
 # HBM bytes of one pa_decode call on decode_bf16 (split kernel plus merge kernel, the same unit
-# the headline times), from two rocprofv3 passes (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a
-# plain 1 GiB copy; the summary is in profiles/pa_decode.all_decode_workloads.md).  They describe
-# the kernel source with this SHA-256 prefix only (pa_decode.hip and decode_item.hpp together);
-# after any change to them the figure is reported as null.
+# the headline times), from two rocprofv3 passes over the headline's cold-cache calls
+# (FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a plain 1 GiB copy; the summary is in
+# profiles/pa_decode.decode_bf16_cold.md).  They describe the kernel source with this SHA-256
+# prefix only (pa_decode.hip and decode_item.hpp together); after any change to them the figure
+# is reported as null.
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_341_amd", "csrc", f)
                for f in ("pa_decode.hip", "decode_item.hpp")]
-MEASURED_TRAFFIC = {"sha256_prefix": "97eb7f0369c61c1f",
-                    "split": {"fetch_kib": 243635.7, "write_kib": 4307.8},
-                    "merge": {"fetch_kib": 4192.5, "write_kib": 456.0},
+MEASURED_TRAFFIC = {"sha256_prefix": "7fe7ed8b5bd08285",
+                    "split": {"fetch_kib": 243514.7, "write_kib": 4308.4},
+                    "merge": {"fetch_kib": 4200.0, "write_kib": 456.0},
                     "fetch_scale": 2.0, "write_scale": 1.0}
 
 
