@@ -230,6 +230,27 @@ def test_decode_over_declared_max_len():
     assert_close(widen(c), widen(a), 1e-6, 1e-6, "max_seq_len slack")
 
 
+def test_decode_native_context_length():
+    """The longest context the pages mention, 262,144 tokens, beside a half-length and a
+    one-token sequence: 512 split slots per row, so the merge takes its general path (more
+    than 64 splits, summed 64 at a time in split order)."""
+    say("case: decode at 262144 tokens (512 splits per row)")
+    b = W.make_decode([262144, 131073, 1], 8, 2, 128, "bf16", seed=1550, device=DEV)
+    n = ops.pa_decode_workspace_size(3, 8, 2, 128, 16, 262144)
+    assert n >= 3 * 8 * 512 * 130 * 4, "expected 512 split slots per row"
+    out = run_decode(b)
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, "decode 262144")
+    for h in range(8):
+        assert torch.equal(out[2, h], b.v_cache[int(b.block_tables[2, 0]), h // 4, 0])
+
+
+def test_prefill_at_native_context_length():
+    """Chunks ending 262,144- and 131,000-token sequences (prefixes of 262,044 and 130,937)."""
+    say("case: prefill chunks over 262k and 131k prefixes")
+    _, out, want = _prefill_case(1560, [100, 63], [262044, 130937], G=4)
+    assert_close(widen(out), want, ATOL, RTOL, "prefill 262k prefix")
+
+
 def test_decode_workspace_reused_across_calls():
     """One uninitialised workspace serves calls of different shapes in turn (short and long
     splits), and every result matches the oracle: no workspace state carries over."""
