@@ -6,8 +6,10 @@ divided by the decode call time) on the 64-sequence decode batch (lengths U[128,
 heads, head_dim 128, bf16 KV).  The same JSON line carries the mixed continuous-batching step
 (KV append of 4288 tokens, eight 512-token prefill chunks over paged prefixes, 192 decodes) as
 tokens/s, the 32 x 32768-token long-context decode, and the beam step (112 copy-on-write block
-copies, tail append, decode of 128 beams), each timed with HIP events on the stream the kernels
-run on.  Inputs are synthetic and already resident in HBM when timing starts.
+copies, tail append, decode of 128 beams), and 24 planned continuous-batching steps (64 decoders
+while a 30,000-token prompt arrives) with and without a per-step token cap, each timed with HIP
+events on the stream the kernels run on.  Inputs are synthetic and already resident in HBM when
+timing starts.
 
 `--gpus N` with N > 1 is refused: this build runs on one GPU.
 """
@@ -459,6 +461,94 @@ def bench_beams(steps, warmup):
     return res
 
 
+def bench_token_cap(cap: int, long_prompt: int = 30000, num_decoders: int = 64,
+                    steps: int = 24, arrive_at: int = 2, seed: int = 3430):
+    """Continuous batching with and without a per-step token cap: `num_decoders` sequences
+    (lengths U[1000, 3000]) decode while a `long_prompt`-token prompt arrives at step
+    `arrive_at`; every step is planned by the native step planner and run as kv_append +
+    pa_prefill_chunk + pa_decode (32/8 heads, D128, bf16, one layer's attention), timed with
+    HIP events around the three calls.  Returns per-step times and the step-time statistics
+    the decoding sequences see (each step gives each of them one token)."""
+    from paged_kv_cache_341_amd.native_block_manager import NativeBlockManager, NativeStepPlanner
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D, B = 32, 8, 128, 16
+    lens = rng.integers(1000, 3001, size=num_decoders)
+    need = sum(-(-int(L) // B) + steps // B + 2 for L in lens) + -(-long_prompt // B) + steps
+    NB = int(need * 1.2)
+    bm = NativeBlockManager(NB, B, free_order=rng.permutation(NB))
+    # warm start: the decoders' prompts in one uncapped step (untimed, no kernels: the pool's
+    # values are random), then the cap under test
+    sp = NativeStepPlanner(bm, 1 << 30)
+    for s_id, L in enumerate(lens):
+        sp.add_request(s_id, int(L))
+    sp.step()
+    sp.set_limits(cap)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn((NB, Hkv, B, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((NB, Hkv, B, D), generator=g, device="cuda").to(torch.bfloat16)
+    scale = W.default_scale(D)
+    stream = torch.cuda.current_stream()
+    times, tokens, chunk_tokens = [], [], []
+    for step in range(steps):
+        if step == arrive_at:
+            sp.add_request(num_decoders, long_prompt)
+        p = sp.step()
+        T = p.num_tokens
+        k_new = torch.randn((T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+        v_new = torch.randn((T, Hkv, D), generator=g, device="cuda").to(torch.bfloat16)
+        sm = i64(p.slot_mapping)
+        C, S = len(p.chunk_seqs), len(p.decode_seqs)
+        if C:
+            ct = bm.block_tables(p.chunk_seqs)
+            cl = np.array([bm.seq_len(x) for x in p.chunk_seqs], np.int32)
+            qsl = p.query_start_loc()
+            checks.check_tables(ct, cl, NB, B, int(cl.max()))
+            checks.check_chunks(qsl, cl, int(qsl[-1]), int(np.diff(qsl).max()))
+            q_c = torch.randn((int(qsl[-1]), Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+            o_c = torch.empty_like(q_c)
+            ct_d, cl_d, qsl_d = i32(ct), i32(cl), i32(qsl)
+        if S:
+            dt = bm.block_tables(p.decode_seqs)
+            dl = np.array([bm.seq_len(x) for x in p.decode_seqs], np.int32)
+            checks.check_tables(dt, dl, NB, B, int(dl.max()))
+            q_d = torch.randn((S, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+            o_d = torch.empty_like(q_d)
+            ws = torch.empty(max(ops.pa_decode_workspace_size(S, Hq, Hkv, D, B, int(dl.max())), 16),
+                             dtype=torch.uint8, device="cuda")
+            dt_d, dl_d = i32(dt), i32(dl)
+        checks.check_slots(p.slot_mapping, NB, B)
+        torch.cuda.synchronize()
+        # the first step runs once untimed before its timed run (the append writes the same
+        # values to the same slots, so the repeat changes nothing): the set-up's idle gap
+        # otherwise lands in step 0
+        for _ in range(2 if step == 0 else 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ops.kv_append(k, v, k_new, v_new, sm)
+            if C:
+                ops.pa_prefill_chunk(o_c, q_c, k, v, ct_d, cl_d, qsl_d, int(np.diff(qsl).max()),
+                                     int(cl.max()), scale)
+            if S:
+                ops.pa_decode(o_d, q_d, k, v, dt_d, dl_d, int(dl.max()), scale, workspace=ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        tokens.append(T)
+        chunk_tokens.append(int(sum(p.chunk_lens)))
+    t = np.array(times)
+    prompt_steps = int(sum(1 for c in chunk_tokens if c > 0))
+    res = {"cap": cap if cap < (1 << 30) else None, "steps": steps,
+           "step_ms": [round(x, 4) for x in times], "tokens_per_step": tokens,
+           "step_ms_median": round(float(np.median(t)), 4), "step_ms_max": round(float(t.max()), 4),
+           "prompt_steps": prompt_steps,
+           "tokens_per_s": round(float(sum(tokens) / (t.sum() * 1e-3)), 1)}
+    log(f"token cap {res['cap']}: step median {res['step_ms_median']:.3f} ms, max "
+        f"{res['step_ms_max']:.3f} ms, prompt prefilled over {prompt_steps} steps, "
+        f"{res['tokens_per_s']:.0f} tokens/s")
+    return res
+
+
 def bench_swap(steps, warmup, num_blocks=2048):
     """Preemption by swapping: `num_blocks` whole blocks (8 kv heads x 16 x 128 bf16, K and V:
     64 KiB each) copied device -> pinned host and back with swap_blocks, the pairs planned by the
@@ -599,7 +689,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip", default="",
-                    help="comma list of: mixed,long,beams,swap,indirection")
+                    help="comma list of: mixed,long,beams,swap,tokencap,indirection")
     ap.add_argument("--overlap-mixed", action="store_true",
                     help="also time the mixed step with chunks and decodes on two streams")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -667,6 +757,10 @@ def main():
         torch.cuda.empty_cache()
     if "swap" not in skip:
         extra["swap"] = bench_swap(5, 2)
+        torch.cuda.empty_cache()
+    if "tokencap" not in skip:
+        extra["token_cap"] = {"capped_2048": bench_token_cap(2048),
+                              "uncapped": bench_token_cap(1 << 30)}
         torch.cuda.empty_cache()
     if "indirection" not in skip:
         extra["indirection"] = indirection_sweep(30)

@@ -181,6 +181,10 @@ typedef struct pa_sp_plan {
 pa_sp* pa_sp_create(pa_bm* bm, int32_t max_tokens_per_step, int32_t max_chunk);
 void pa_sp_destroy(pa_sp* sp);
 
+/* Change the cap and the per-request chunk limit from the next step on (same rules as
+ * pa_sp_create). */
+pa_bm_status pa_sp_set_limits(pa_sp* sp, int32_t max_tokens_per_step, int32_t max_chunk);
+
 /* Queue a new prompt of prompt_len (> 0) tokens; its sequence must not exist yet. */
 pa_bm_status pa_sp_add_request(pa_sp* sp, int64_t seq_id, int64_t prompt_len);
 

@@ -505,6 +505,14 @@ pa_sp* pa_sp_create(pa_bm* bm, int32_t max_tokens_per_step, int32_t max_chunk) {
 
 void pa_sp_destroy(pa_sp* sp) { delete sp; }
 
+pa_bm_status pa_sp_set_limits(pa_sp* sp, int32_t max_tokens_per_step, int32_t max_chunk) {
+  if (!sp || max_tokens_per_step <= 0 || max_chunk < 0)
+    return bm_fail(PA_BM_INVALID, "pa_sp_set_limits: need a positive cap and max_chunk >= 0");
+  sp->max_tokens = max_tokens_per_step;
+  sp->max_chunk = max_chunk;
+  return bm_ok();
+}
+
 pa_bm_status pa_sp_add_request(pa_sp* sp, int64_t seq_id, int64_t prompt_len) {
   if (!sp || prompt_len <= 0)
     return bm_fail(PA_BM_INVALID, "pa_sp_add_request: a prompt holds at least one token");

@@ -64,6 +64,7 @@ def _bind(lib):
         "pa_bm_last_error": (ctypes.c_char_p, []),
         "pa_sp_create": (_vp, [_vp, _i32, _i32]),
         "pa_sp_destroy": (None, [_vp]),
+        "pa_sp_set_limits": (ctypes.c_int, [_vp, _i32, _i32]),
         "pa_sp_add_request": (ctypes.c_int, [_vp, _i64, _i64]),
         "pa_sp_finish": (ctypes.c_int, [_vp, _i64]),
         "pa_sp_counts": (ctypes.c_int, [_vp, _P32, _P32]),
@@ -300,6 +301,11 @@ class NativeStepPlanner:
         d, p = ctypes.c_int32(), ctypes.c_int32()
         self.bm._check(_lib().pa_sp_counts(self._h, ctypes.byref(d), ctypes.byref(p)))
         return d.value, p.value
+
+    def set_limits(self, max_tokens_per_step: int, max_chunk: Optional[int] = None) -> None:
+        self.bm._check(_lib().pa_sp_set_limits(self._h, int(max_tokens_per_step),
+                                               0 if max_chunk is None else int(max_chunk)))
+        self.max_tokens = int(max_tokens_per_step)
 
     def add_request(self, seq_id: int, prompt_len: int) -> None:
         self.bm._check(_lib().pa_sp_add_request(self._h, int(seq_id), int(prompt_len)))

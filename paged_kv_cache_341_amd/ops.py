@@ -36,7 +36,7 @@ BM_EXPORTED = ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_sequence", "pa_bm_app
                "pa_bm_table", "pa_bm_block_tables", "pa_bm_refcount", "pa_bm_preempt_latest",
                "pa_bm_swap_in_earliest", "pa_bm_resume_recompute", "pa_bm_request_members",
                "pa_bm_get_stats", "pa_bm_last_error", "pa_sp_create", "pa_sp_destroy",
-               "pa_sp_add_request", "pa_sp_finish", "pa_sp_counts", "pa_sp_step")
+               "pa_sp_set_limits", "pa_sp_add_request", "pa_sp_finish", "pa_sp_counts", "pa_sp_step")
 
 
 class PagedAttnError(RuntimeError):

@@ -96,6 +96,13 @@ class StepPlanner:
         self.prefilling: "OrderedDict[int, int]" = OrderedDict()   # seq -> prompt tokens left
         self.decoding: List[int] = []
 
+    def set_limits(self, max_tokens_per_step: int, max_chunk: Optional[int] = None) -> None:
+        """Change the cap and the per-request chunk limit from the next step on."""
+        if max_tokens_per_step <= 0 or (max_chunk is not None and max_chunk <= 0):
+            raise ValueError("max_tokens_per_step and max_chunk must be positive")
+        self.max_tokens = int(max_tokens_per_step)
+        self.max_chunk = None if max_chunk is None else int(max_chunk)
+
     def add_request(self, seq_id: int, prompt_len: int) -> None:
         """A new prompt joins the queue (arrival order); its blocks come with its chunks."""
         if prompt_len <= 0:

@@ -185,6 +185,24 @@ def test_native_matches_python(seed):
             assert [py_bm.seq_len(s) for s in live] == [na_bm.seq_len(s) for s in live]
 
 
+@pytest.mark.parametrize("kind,BM,SP", MANAGERS, ids=[m[0] for m in MANAGERS])
+def test_limits_change_between_steps(kind, BM, SP):
+    """An uncapped first step admits every prompt whole; after set_limits the next prompt is cut
+    to the new cap minus the decodes."""
+    bm = BM(2048, 16)
+    sp = SP(bm, 1 << 30)
+    for s in range(4):
+        sp.add_request(s, 1000 + s)
+    p = sp.step()
+    assert p.chunk_lens == [1000, 1001, 1002, 1003]
+    sp.set_limits(64)
+    sp.add_request(9, 500)
+    p = sp.step()
+    assert p.decode_seqs == [0, 1, 2, 3] and p.chunk_seqs == [9] and p.chunk_lens == [60]
+    with pytest.raises(ValueError):
+        sp.set_limits(0)
+
+
 @pytest.mark.skipif(not HAVE_NATIVE, reason="libpagedattn.so not built")
 def test_native_refuses_bad_arguments():
     bm = NativeBlockManager(16, 16)
