@@ -4,6 +4,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "launch.hpp"
 
 namespace pa {
 
@@ -130,7 +131,7 @@ __device__ __forceinline__ void store_out(bf16_t* p, float v) {
 
 // One split of one (sequence, kv head): `Waves` waves of the calling workgroup share it, and
 // every one of them must make the call (it synchronises the workgroup).  `smem` holds
-// max(bps * B * G, Waves * G * D) floats (scores, then the waves' partial outputs), `red`
+// max(plan.max_units() * B * G, Waves * G * D) floats (scores, then the waves' partial outputs), `red`
 // Waves x G floats, `stat_m` and `stat_l` G floats each.
 // `Batch` blocks per wave are loaded together before their math (0: 64 tokens' worth).
 // With `Prio`, the K phase runs at wave priority 2 and the V phase at 0, each one band higher
@@ -141,7 +142,8 @@ __device__ __forceinline__ void decode_split_item(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     Rows rows, int L, const int32_t* __restrict__ skip_blocks, int slot_base,
-    int num_kv_heads, int bps, int nsplit_max, float scale_log2, int s, int kvh, int split,
+    int num_kv_heads, SplitPlan plan, int nsplit_max, float scale_log2, int s, int kvh,
+    int split,
     float* smem, float (*red)[G], float* stat_m, float* stat_l, bool late = false) {
   using S = DecodeShape<T, D, G, B>;
   constexpr int kBlock = B;
@@ -150,16 +152,16 @@ __device__ __forceinline__ void decode_split_item(
   constexpr int kCpr = S::kCpr;
   constexpr int kThreadsW = Waves * kWave;
   const T tag{};
-  float* logits = smem;                                  // [bps*16][G]
+  float* logits = smem;                                  // [split tokens][G]
 
   const int nblk = (L + kBlock - 1) / kBlock;
   // leading blocks another kernel covers (a prefix shared with the sequence's group)
   const int skip = skip_blocks ? min(max(skip_blocks[s], 0), L / kBlock) : 0;
-  const int b_begin = skip + split * bps;
+  const int b_begin = skip + plan.start(split);
   if (b_begin >= nblk) return;
-  const int b_end = min(nblk, b_begin + bps);
+  const int b_end = min(nblk, skip + plan.start(split + 1));
   const int ntok = min(L, b_end * kBlock) - b_begin * kBlock;
-  const int nsplit_seq = (nblk - skip + bps - 1) / bps;
+  const int nsplit_seq = plan.count(nblk - skip);
   const bool direct = skip == 0 && nsplit_seq == 1;   // the whole sequence in this split
   const int wave = wave_uniform(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;

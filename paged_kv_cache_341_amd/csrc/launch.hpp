@@ -8,6 +8,37 @@
 
 namespace pa {
 
+// How a sequence's units are cut into decode splits: c0 splits of s0 units, then c1 splits of
+// s1 units, then splits of s2 units to the end, with s0 >= s1 >= s2 (a uniform plan has one
+// size).  Split j covers units [start(j), start(j + 1)) of the sequence, clamped to its length.
+// Every workgroup of split index j is launched after all of index j - 1, so shrinking sizes put
+// the smallest pieces last.
+struct SplitPlan {
+  int s0, c0, s1, c1, s2;
+  __host__ __device__ static SplitPlan uniform(int units) { return {units, 0, units, 0, units}; }
+  __host__ __device__ int start(int j) const {
+    const int a = j < c0 ? j : c0;
+    const int b = j - c0 < 0 ? 0 : (j - c0 < c1 ? j - c0 : c1);
+    const int c = j - c0 - c1 < 0 ? 0 : j - c0 - c1;
+    return a * s0 + b * s1 + c * s2;
+  }
+  // number of splits that cover n units
+  __host__ __device__ int count(int n) const {
+    if (n <= 0) return 0;
+    const int e0 = c0 * s0;
+    if (n <= e0) return (n + s0 - 1) / s0;
+    const int e1 = e0 + c1 * s1;
+    if (n <= e1) return c0 + (n - e0 + s1 - 1) / s1;
+    return c0 + c1 + (n - e1 + s2 - 1) / s2;
+  }
+  __host__ __device__ int max_units() const {
+    int m = s2;
+    if (c1 > 0 && s1 > m) m = s1;
+    if (c0 > 0 && s0 > m) m = s0;
+    return m;
+  }
+};
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -28,9 +59,10 @@ struct DecodeArgs {
   int capacity;
   // block_size: tokens per pool block.  The split walk goes in units of block_size tokens, or of
   // 16 tokens when blocks are smaller than 8 (each token's block is then looked up on its own)
-  // and for contiguous KV; bps counts units.
+  // and for contiguous KV; the plan counts units.
   int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
-  int bps, nsplit_max;
+  SplitPlan plan;
+  int nsplit_max;
   float scale_log2;
   bool bf16;
   hipStream_t stream;

@@ -7,7 +7,8 @@
 // h / G, G = Hq / Hkv, so the G query heads of one kv head share every K/V byte read.
 //
 // Work split (our design, not from the pages): one workgroup of 4 waves per
-// (sequence, kv head, split), a split being `bps` consecutive logical blocks.  Inside a split:
+// (sequence, kv head, split), a split being a run of consecutive logical blocks (its length
+// set by the host's split plan, which may shrink toward the later splits).  Inside a split:
 //   phase 1  each wave takes every 4th block, reads its K slab (16 x D contiguous elements),
 //            computes the G scores of every token with lanes split over the head dimension
 //            (DPP sums), and parks them in LDS;
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ skip_blocks, int slot_base, int num_kv_heads,
-    int max_blocks_per_seq, int capacity, int bps, int nsplit_max, float scale_log2) {
+    int max_blocks_per_seq, int capacity, SplitPlan plan, int nsplit_max, float scale_log2) {
   extern __shared__ float smem[];
   __shared__ float red[kDecodeWaves][G];
   __shared__ float stat_m[G];
@@ -59,21 +60,21 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
                                        static_cast<size_t>(capacity) * D};
     decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
         out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
-        bps, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        plan, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
         stat_l, late);
   } else if constexpr (BT == U) {
     const PagedRows<T, D, U> rows{block_tables + static_cast<size_t>(s) * max_blocks_per_seq,
                                   num_kv_heads, kvh};
     decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
         out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
-        bps, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        plan, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
         stat_l, late);
   } else {
     const PagedSmallRows<T, D, U, BT> rows{
         block_tables + static_cast<size_t>(s) * max_blocks_per_seq, num_kv_heads, kvh, L};
     decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
         out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
-        bps, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        plan, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
         stat_l, late);
   }
 }
@@ -88,10 +89,10 @@ template <typename T, int D, int B>
 __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
     T* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ skip_blocks,
-    int slot_base, int shared_split_keys, int num_rows, int num_q_heads, int bps,
+    int slot_base, int shared_split_keys, int num_rows, int num_q_heads, SplitPlan plan,
     int nsplit_max) {
   constexpr int kPer = D / kWave;
-  constexpr int kFast = 8;
+  constexpr int kFast = 16;
   const int row = blockIdx.x * kMergeWaves + static_cast<int>(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   if (row >= num_rows) return;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
     const float mraw = lane < nsplit_max ? ml[2 * lane] : 0.f;
     const float lraw = lane < nsplit_max ? ml[2 * lane + 1] : 0.f;
     const int L = seq_lens[s];
-    const int nsplit = ((L + B - 1) / B + bps - 1) / bps;
+    const int nsplit = plan.count((L + B - 1) / B);
     if (nsplit <= 1) return;                      // written directly by the split kernel
     const float mi = lane < nsplit ? mraw : kNegInf;
     const float li = lane < nsplit ? lraw : 0.f;
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   // start there, so they form one range
   const int skip = skip_blocks ? min(max(skip_blocks[s], 0), L / B) : 0;
   const int ns = skip > 0 ? (skip * B + shared_split_keys - 1) / shared_split_keys : 0;
-  const int nt = (nblk - skip + bps - 1) / bps;
+  const int nt = plan.count(nblk - skip);
   if (ns == 0 && nt <= 1) return;                 // written directly by the split kernel
   const int nsplit = ns + nt;
   const float* ml = ws_ml + (static_cast<size_t>(row) * nsplit_max + slot_base - ns) * 2;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
 
 template <typename T, int D, int G, int U, int BT, bool Contig>
 hipError_t launch_decode_tb(const DecodeArgs& a) {
-  const size_t lds = std::max<size_t>(static_cast<size_t>(a.bps) * U * G,
+  const size_t lds = std::max<size_t>(static_cast<size_t>(a.plan.max_units()) * U * G,
                                       static_cast<size_t>(kDecodeWaves) * G * D) * sizeof(float);
   const dim3 grid_split(a.num_seqs * a.num_kv_heads, a.nsplit_tail);
   hipLaunchKernelGGL((pa_decode_split_kernel<T, D, G, U, BT, Contig>), grid_split,
@@ -228,14 +229,14 @@ hipError_t launch_decode_tb(const DecodeArgs& a) {
                      a.ws_acc, static_cast<const T*>(a.q), static_cast<const T*>(a.k_cache),
                      static_cast<const T*>(a.v_cache), a.block_tables, a.seq_lens,
                      a.skip_blocks, a.slot_base, a.num_kv_heads, a.max_blocks_per_seq,
-                     a.capacity, a.bps, a.nsplit_max, a.scale_log2);
+                     a.capacity, a.plan, a.nsplit_max, a.scale_log2);
   if (a.nsplit_max > 1) {
     const int rows = a.num_seqs * a.num_kv_heads * G;
     hipLaunchKernelGGL((pa_decode_merge_kernel<T, D, U>),
                        dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
                        a.stream, static_cast<T*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens,
                        a.skip_blocks, a.slot_base, a.shared_split_keys, rows,
-                       a.num_kv_heads * G, a.bps, a.nsplit_max);
+                       a.num_kv_heads * G, a.plan, a.nsplit_max);
   }
   return hipGetLastError();
 }
@@ -247,8 +248,8 @@ hipError_t launch_decode_merge(const DecodeArgs& a) {
   hipLaunchKernelGGL((pa_decode_merge_kernel<bf16_t, 128, 16>),
                      dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
                      a.stream, static_cast<bf16_t*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens,
-                     a.skip_blocks, a.slot_base, a.shared_split_keys, rows, a.num_q_heads, a.bps,
-                     a.nsplit_max);
+                     a.skip_blocks, a.slot_base, a.shared_split_keys, rows, a.num_q_heads,
+                     a.plan, a.nsplit_max);
   return hipGetLastError();
 }
 

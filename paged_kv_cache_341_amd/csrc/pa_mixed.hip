@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
           dec_tables + static_cast<size_t>(s) * dec_max_blocks, num_kv_heads, kvh};
       decode_split_item<bf16_t, kD, G, kBlock, kWaves, kMixedDecodeBatch>(
           dec_out, ws_ml, ws_acc, dec_q, k_cache, v_cache, rows, dec_seq_lens[s], nullptr, 0,
-          num_kv_heads, bps, nsplit_max, scale_log2, s, kvh, split,
+          num_kv_heads, SplitPlan::uniform(bps), nsplit_max, scale_log2, s, kvh, split,
           reinterpret_cast<float*>(ring), dred, dstat_m, dstat_l);
     }
     __syncthreads();                               // the ring is reused by the next item

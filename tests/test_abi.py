@@ -102,6 +102,24 @@ def test_decode_noalloc_scratch_size_matches_header():
     assert m and int(m.group(1)) << int(m.group(2)) == ops.DECODE_NOALLOC_SCRATCH_BYTES
 
 
+def _slots(size, rows, head_dim):
+    for n in range(1, 4096):
+        if (rows * n * 8 + 255) // 256 * 256 + rows * n * head_dim * 4 == size:
+            return n
+    raise AssertionError(size)
+
+
+def test_decode_split_plans():
+    """The split plan behind the workspace size: shrinking sizes (64, 32, 32, then 16 blocks)
+    for 64 sequences of up to 4096 tokens; one size for a batch whose grid fits the chip about
+    once (8 sequences: 16 splits of 16 blocks) and for 32 sequences of 32768 tokens (32 splits
+    of 64 blocks); 256 sequences of up to 4096 tokens: 128, 64 and 64 blocks."""
+    assert _slots(ops.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096), 64 * 32, 128) == 11
+    assert _slots(ops.pa_decode_workspace_size(8, 32, 8, 128, 16, 4096), 8 * 32, 128) == 16
+    assert _slots(ops.pa_decode_workspace_size(32, 16, 4, 256, 16, 32768), 32 * 16, 256) == 32
+    assert _slots(ops.pa_decode_workspace_size(256, 32, 8, 128, 16, 4096), 256 * 32, 128) == 3
+
+
 def test_decode_workspace_sizes():
     # one split: no workspace; long sequences: partials for every split
     assert ops.pa_decode_workspace_size(4, 2, 1, 64, 16, 100) == 0

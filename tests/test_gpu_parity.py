@@ -271,19 +271,28 @@ def test_decode_workspace_reused_across_calls():
         assert_close(widen(out), oracle_decode(x), ATOL, RTOL, "reused workspace")
 
 
+def split_slots(size, rows, head_dim):
+    """Split slots per row of a decode workspace of `size` bytes (statistics block rounded up
+    to 256 bytes, then the partial numerators)."""
+    for n in range(1, 4096):
+        if (rows * n * 8 + 255) // 256 * 256 + rows * n * head_dim * 4 == size:
+            return n
+    raise AssertionError(f"no slot count gives {size} bytes")
+
+
 def test_decode_merge_ignores_unused_workspace_slots():
-    """Rows with fewer splits than the workspace has slots (at most 8 slots per row: the merge
+    """Rows with fewer splits than the workspace has slots (up to 16 slots per row: the merge
     requests every slot before it knows the row's split count) must ignore the unused slots:
-    the workspace is filled with NaN bit patterns before the call."""
-    say("case: decode with a NaN-filled workspace, 1..8 splits per row")
+    the workspace is filled with NaN bit patterns before the call.  The batch's split plan has
+    sizes that shrink toward the later splits (11 slots for a 4096-token row)."""
+    say("case: decode with a NaN-filled workspace, 1..11 splits per row")
     lens = [1, 15, 16, 17, 511, 512, 513, 1024, 1500, 2049, 3000, 4095, 4096]
     lens += list(range(100, 4096, 150))[:27]
     b = W.make_decode(lens, 32, 8, 128, "bf16", seed=960, device=DEV)
     size = ops.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
                                         16, b.max_seq_len)
     rows = b.num_seqs * b.num_q_heads
-    ml_bytes = (rows * 8 * 2 * 4 + 255) // 256 * 256
-    assert size == ml_bytes + rows * 8 * 128 * 4, "the batch should plan 8 split slots per row"
+    assert split_slots(size, rows, 128) == 11, "the batch should plan 11 split slots per row"
     ws = torch.empty(size, dtype=torch.uint8, device=DEV).fill_(0xFF)
     bt, sl = dev_i32(b.block_tables), dev_i32(b.seq_lens)
     out = torch.empty_like(b.q)
