@@ -46,9 +46,9 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 # is reported as null.
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_341_amd", "csrc", f)
                for f in ("pa_decode.hip", "decode_item.hpp")]
-MEASURED_TRAFFIC = {"sha256_prefix": "7fe7ed8b5bd08285",
-                    "split": {"fetch_kib": 243514.7, "write_kib": 4308.4},
-                    "merge": {"fetch_kib": 4200.0, "write_kib": 456.0},
+MEASURED_TRAFFIC = {"sha256_prefix": "05fd985c73365828",
+                    "split": {"fetch_kib": 243523.2, "write_kib": 4075.7},
+                    "merge": {"fetch_kib": 5786.0, "write_kib": 336.0},
                     "fetch_scale": 2.0, "write_scale": 1.0}
 
 
