@@ -139,7 +139,7 @@ pa_status pa_decode_contiguous(void* out, const void* q, const void* k, const vo
  *   Errors:  those of pa_decode, and PA_ERR_DEVICE if the array's address cannot be obtained on
  *            the current device.
  */
-#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* seq_lens,
                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

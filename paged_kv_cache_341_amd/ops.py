@@ -221,7 +221,7 @@ def pa_decode_contiguous(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v:
 
 # Bytes of the library's static scratch behind pa_decode_noalloc (PA_DECODE_NOALLOC_SCRATCH_BYTES
 # in pagedattn.h).
-DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+DECODE_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def pa_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
