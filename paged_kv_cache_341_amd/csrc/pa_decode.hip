@@ -99,23 +99,24 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void pa_decode_merge_kernel(
   const int s = row / num_q_heads;
 
   if (skip_blocks == nullptr && slot_base == 0 && nsplit_max <= kFast) {
-    // Plain decode with at most kFast split slots per row: every slot of the row exists in the
-    // workspace, so its statistics and partials are requested together with the sequence
-    // length (one round trip instead of two); slots past the row's split count are dropped by
-    // selection, never used.
+    // Plain decode with at most kFast split slots per row: the row's split count follows from
+    // the sequence length, then the statistics and partials of exactly those splits are
+    // requested together (one round trip).  Reading every slot of the row with the length
+    // instead saves that dependent load but fetches the unused slots too; with the shrinking
+    // split plans (11 slots for 4096-token rows, 5 used on average) that cost more.
     const float* ml = ws_ml + static_cast<size_t>(row) * nsplit_max * 2;
     const float* acc = ws_acc + static_cast<size_t>(row) * nsplit_max * D;
-    float a[kFast][kPer];
-#pragma unroll
-    for (int u = 0; u < kFast; ++u)
-      if (u < nsplit_max)
-#pragma unroll
-        for (int e = 0; e < kPer; ++e) a[u][e] = acc[static_cast<size_t>(u) * D + lane + e * kWave];
-    const float mraw = lane < nsplit_max ? ml[2 * lane] : 0.f;
-    const float lraw = lane < nsplit_max ? ml[2 * lane + 1] : 0.f;
     const int L = seq_lens[s];
     const int nsplit = plan.count((L + B - 1) / B);
     if (nsplit <= 1) return;                      // written directly by the split kernel
+    float a[kFast][kPer];
+#pragma unroll
+    for (int u = 0; u < kFast; ++u)
+      if (u < nsplit)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a[u][e] = acc[static_cast<size_t>(u) * D + lane + e * kWave];
+    const float mraw = lane < nsplit ? ml[2 * lane] : 0.f;
+    const float lraw = lane < nsplit ? ml[2 * lane + 1] : 0.f;
     const float mi = lane < nsplit ? mraw : kNegInf;
     const float li = lane < nsplit ? lraw : 0.f;
     const float Mf = group_max<kWave>(mi);
