@@ -86,6 +86,46 @@ def test_decode_other_block_sizes(B):
     assert_close(widen(run_decode(f)), oracle_decode(f), F32_ATOL, F32_RTOL, f"f32 B{B}")
 
 
+def _shrinking_plan_slots(max_len, G, unit):
+    """Split slots of the shrinking plan the library picks for 64 sequences x 8 kv heads of up
+    to max_len tokens: b = 512 tokens per split (capped at 8192 / G tokens), n = ceil(units / b),
+    then max(1, n / 8) splits of 2b, two of b, then b / 2."""
+    b = min(512 // unit, 8192 // G // unit)
+    nb = -(-max_len // unit)
+    n = -(-nb // b)
+    assert 3 <= n <= 16 and 64 * 8 * n >= 2048
+    s0, c0, s1, c1, s2 = min(2 * b, 8192 // G // unit), max(1, n // 8), b, 2, b // 2
+    if nb <= c0 * s0:
+        return -(-nb // s0)
+    if nb <= c0 * s0 + c1 * s1:
+        return c0 + -(-(nb - c0 * s0) // s1)
+    return c0 + c1 + -(-(nb - c0 * s0 - c1 * s1) // s2)
+
+
+@pytest.mark.parametrize("G,D,dtype,B", [(1, 64, "bf16", 16), (2, 256, "bf16", 16),
+                                         (8, 128, "bf16", 16), (2, 128, "f32", 32),
+                                         (4, 128, "bf16", 8), (4, 64, "bf16", 1)])
+def test_decode_shrinking_split_plans(G, D, dtype, B):
+    """64 sequences x 8 kv heads of up to 4096 tokens take split sizes that shrink toward the
+    last splits (checked through the workspace size); every row against the oracle, with
+    lengths on the plan's split edges and NaN in every unfilled slot."""
+    say(f"case: shrinking split plan G={G} D={D} {dtype} B={B}")
+    rng = np.random.default_rng(2600 + G + D + B)
+    edges = [1, 16, 17, 1023, 1024, 1025, 1536, 1537, 2048, 2049, 3072, 4095, 4096]
+    lens = edges + rng.integers(1, 4097, size=64 - len(edges)).tolist()
+    b = W.make_decode(lens, 8 * G, 8, D, dtype, seed=2600 + G + D + B, device=DEV,
+                      block_size=B)
+    unit = B if B >= 8 else 16
+    size = ops.pa_decode_workspace_size(64, 8 * G, 8, D, B, 4096)
+    assert split_slots(size, 64 * 8 * G, D) == _shrinking_plan_slots(4096, G, unit)
+    out = run_decode(b)
+    atol, rtol = (ATOL, RTOL) if dtype == "bf16" else (F32_ATOL, F32_RTOL)
+    assert_close(widen(out), oracle_decode(b), atol, rtol, f"plan G{G} D{D} {dtype} B{B}")
+    tab = int(b.block_tables[0, 0])
+    for h in range(8 * G):
+        assert torch.equal(out[0, h], b.v_cache[tab, h // G, 0])
+
+
 def test_decode_bf16_full_batch():
     """The 64-sequence batch at full size, every element against the oracle; then ten more
     calls that must each give the first call's bits (run-to-run identity)."""
