@@ -200,7 +200,7 @@ size_t pa_decode_grouped_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   max_seq_len     host upper bound of seq_lens
  *   scale           multiplies q.k before the softmax; finite and > 0
  *
- * Supported: dtype BF16 (MFMA bf16 -> fp32), head_dim 128, block_size 16,
+ * Supported: dtype BF16 (MFMA bf16 -> fp32), head_dim 64, 128 or 256, block_size 16,
  * num_q_heads/num_kv_heads in {1, 2, 4, 8}.  Needs no workspace.  Up to 128 chunks are
  * scheduled longest first (ranked on the device from seq_lens); more are taken in order.
  */

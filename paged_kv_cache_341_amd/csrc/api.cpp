@@ -739,8 +739,9 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_prefill_chunk: scale must be finite and positive");
   if (dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: only bf16 is supported");
-  if (head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: head_dim %d (supported: 128)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: head_dim %d (supported: 64, 128, 256)",
+                head_dim);
   if (block_size != kSupportedBlock)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: block_size %d (supported: 16)",
                 block_size);
@@ -748,10 +749,12 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   if (!supported_group(g))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: %d query heads per kv head "
                 "(supported: 1,2,4,8)", g);
-  // one workgroup of 512 lanes per (chunk, row tile of 256 rows, kv head); rows are
-  // (token, query head) pairs
+  // one workgroup per (chunk, row tile, kv head): row tiles of 256 rows (128 at head_dim 256);
+  // rows are (token, query head) pairs
+  const int64_t tile_rows = head_dim == 256 ? 128 : 256;
   const int64_t tiles_max =
-      (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + 255) / 256;
+      (static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads) + tile_rows - 1) /
+      tile_rows;
   if (static_cast<int64_t>(num_chunks) * tiles_max * num_kv_heads > (int64_t{1} << 24))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk: grid too large");
   PA_CHECK_CONTENTS("pa_prefill_chunk",

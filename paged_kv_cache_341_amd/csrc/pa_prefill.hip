@@ -11,6 +11,10 @@
 //   * A work item is (chunk, row tile, kv head).  Rows of a tile are (token, query head) pairs
 //     with the G heads of one kv head innermost, so the G heads share every K/V tile.  A
 //     workgroup owns 256 rows: 8 waves x 32 rows, one workgroup per CU (two waves per SIMD).
+//     That is the shape for head_dim 128 described below, and for head_dim 64 with half-width
+//     tiles; at head_dim 256 a workgroup owns 128 rows (4 waves, one per SIMD, whose
+//     accumulators and Q operand need more than half a SIMD's registers) and tiles hold 32
+//     keys (PfShape in prefill_item.hpp).
 //   * Items are dealt longest chunk first (ranked inside the kernel from seq_lens, no host
 //     read-back), last row tile first within a chunk, kv head fastest.  Workgroups reach the 8
 //     XCDs round-robin in launch order, so with 8 kv heads each XCD serves one head, and the
@@ -39,26 +43,27 @@
 
 namespace pa {
 
-template <int G>
-__global__ __launch_bounds__(kThreads, 1) void pa_prefill_kernel(
+template <int G, int D>
+__global__ __launch_bounds__(PfShape<D>::kThreads, 1) void pa_prefill_kernel(
     bf16_t* __restrict__ out, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_start_loc,
     int num_chunks, int num_kv_heads, int max_blocks_per_seq, int tiles_max, float scale_log2) {
-  // A 4-stage ring of K and V tiles, as distinct arrays (128 KiB).  The loop is unrolled by
-  // four so every access names its stage at compile time, which lets the compiler see that
-  // the loads into one stage cannot alias the reads of another.
-  __shared__ uint4 sK0[kKvTile * kChunks], sK1[kKvTile * kChunks], sK2[kKvTile * kChunks],
-      sK3[kKvTile * kChunks];
-  __shared__ uint4 sV0[kKvTile * kChunks], sV1[kKvTile * kChunks], sV2[kKvTile * kChunks],
-      sV3[kKvTile * kChunks];
+  // A 4-stage ring of K and V tiles, as distinct arrays (128 KiB; 64 KiB at head_dim 64).  The
+  // loop is unrolled by four so every access names its stage at compile time, which lets the
+  // compiler see that the loads into one stage cannot alias the reads of another.
+  using Sh = PfShape<D>;
+  static_assert(Sh::kThreads >= kRankCap, "the in-kernel ranking gives one chunk per thread");
+  __shared__ uint4 sK0[Sh::kRing], sK1[Sh::kRing], sK2[Sh::kRing], sK3[Sh::kRing];
+  __shared__ uint4 sV0[Sh::kRing], sV1[Sh::kRing], sV2[Sh::kRing], sV3[Sh::kRing];
   __shared__ PrefillRank rk;
 
   const int w = blockIdx.x;
   int c, tile, kvh;
   if (num_chunks <= kRankCap) {
-    prefill_rank<G>(rk, seq_lens, query_start_loc, num_chunks, num_kv_heads);
-    if (!prefill_locate<G>(rk, w, query_start_loc, num_chunks, num_kv_heads, c, tile, kvh))
+    prefill_rank<G, Sh::kTileRows>(rk, seq_lens, query_start_loc, num_chunks, num_kv_heads);
+    if (!prefill_locate<G, Sh::kTileRows>(rk, w, query_start_loc, num_chunks, num_kv_heads, c,
+                                          tile, kvh))
       return;                                            // past the last item
   } else {
     c = w / (tiles_max * num_kv_heads);
@@ -66,21 +71,33 @@ __global__ __launch_bounds__(kThreads, 1) void pa_prefill_kernel(
     tile = rem / num_kv_heads;
     kvh = rem % num_kv_heads;
   }
-  prefill_item<G>(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+  prefill_item<G, D>(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
                   num_kv_heads, max_blocks_per_seq, scale_log2, c, tile, kvh, sK0, sK1, sK2, sK3,
                   sV0, sV1, sV2, sV3);
 }
 
-template <int G>
-static hipError_t launch_prefill_g(const PrefillArgs& a) {
-  const int tiles_max = (a.max_q_len * G + kTileRows - 1) / kTileRows;
+template <int G, int D>
+static hipError_t launch_prefill_gd(const PrefillArgs& a) {
+  using Sh = PfShape<D>;
+  const int tiles_max = (a.max_q_len * G + Sh::kTileRows - 1) / Sh::kTileRows;
   const int64_t items = static_cast<int64_t>(a.num_chunks) * tiles_max * a.num_kv_heads;
-  hipLaunchKernelGGL((pa_prefill_kernel<G>), dim3(static_cast<unsigned>(items)), dim3(kThreads),
+  hipLaunchKernelGGL((pa_prefill_kernel<G, D>), dim3(static_cast<unsigned>(items)),
+                     dim3(Sh::kThreads),
                      0, a.stream, static_cast<bf16_t*>(a.out), static_cast<const bf16_t*>(a.q),
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.v_cache),
                      a.block_tables, a.seq_lens, a.query_start_loc, a.num_chunks,
                      a.num_kv_heads, a.max_blocks_per_seq, tiles_max, a.scale_log2);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_prefill_g(const PrefillArgs& a) {
+  switch (a.head_dim) {
+    case 64: return launch_prefill_gd<G, 64>(a);
+    case 128: return launch_prefill_gd<G, 128>(a);
+    case 256: return launch_prefill_gd<G, 256>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

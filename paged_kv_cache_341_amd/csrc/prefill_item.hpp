@@ -22,6 +22,39 @@ constexpr float kLazyLog2 = 8.f;                    // rescale only past 2^8 gro
 
 }  // namespace
 
+// The work-item shape for head_dim D (the constants above are D = 128's).  D 64 and 128: eight
+// waves of 32 rows, 64-key tiles.  D 256: its fp32 accumulators (128 per lane) and Q operand do
+// not fit two waves per SIMD, so four waves of 32 rows (one per SIMD) and 32-key tiles, which
+// keep the 4-stage ring at 128 KiB.  In every shape half the waves stage K and half V, one
+// 16-token block each per tile.
+template <int D>
+struct PfShape {
+  static constexpr int kD = D;
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kWaves = D == 256 ? 4 : 8;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kTileRows = kWaves * kRowsPerWave;
+  static constexpr int kKvTile = D == 256 ? 32 : 64;      // keys per LDS tile
+  static constexpr int kKeySub = kKvTile / 32;           // 32-key score tiles per LDS tile
+  static constexpr int kPvSteps = kKvTile / 16;          // 16-key P.V products per d tile
+  static constexpr int kLoads = kBlock * D * 2 / 1024;   // 1 KiB loads per staged block
+  static constexpr int kKeysPerLoad = kWave / kChunks;
+  static constexpr int kRing = kKvTile * kChunks;        // uint4 per K or V ring stage
+  static constexpr int kChunkBits = kChunks == 8 ? 3 : kChunks == 16 ? 4 : 5;
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  static_assert(kWaves / 2 == kKvTile / kBlock, "one wave stages each K and each V block");
+  // Swizzles of the row-major tiles (16-byte chunks of a key row): K rows are read one chunk per
+  // lane down 32 keys, V rows four keys at a time by the transposing load.  For D = 128 these
+  // are k_swz and v_swz.
+  static __device__ __forceinline__ int kswz(int key, int chunk) {
+    return chunk ^ (key & (kChunks - 1));
+  }
+  static __device__ __forceinline__ int vswz(int key, int chunk) {
+    return chunk ^ ((key & 3) << (kChunkBits - 2));
+  }
+};
+
 // Longest-first order of up to kRankCap chunks, kept in LDS: chunk c's items occupy
 // [end[c] - items[c], end[c]) of the item sequence, chunks ranked by length (descending, ties
 // by index); within a chunk the last row tile comes first and the kv head varies fastest.
@@ -33,8 +66,9 @@ struct PrefillRank {
   int item[2];
 };
 
-// Every thread of the workgroup calls this (it synchronises); num_chunks <= kRankCap.
-template <int G>
+// Every thread of the workgroup calls this (it synchronises); num_chunks <= kRankCap, and the
+// workgroup has at least kRankCap threads.
+template <int G, int TileRows = kTileRows>
 __device__ __forceinline__ void prefill_rank(PrefillRank& rk, const int32_t* __restrict__ seq_lens,
                                              const int32_t* __restrict__ query_start_loc,
                                              int num_chunks, int num_kv_heads) {
@@ -43,7 +77,7 @@ __device__ __forceinline__ void prefill_rank(PrefillRank& rk, const int32_t* __r
   if (tid < num_chunks) {
     my_len = seq_lens[tid];
     const int n = query_start_loc[tid + 1] - query_start_loc[tid];
-    my_items = (n * G + kTileRows - 1) / kTileRows * num_kv_heads;
+    my_items = (n * G + TileRows - 1) / TileRows * num_kv_heads;
     rk.len[tid] = my_len;
     rk.items[tid] = my_items;
   }
@@ -70,7 +104,7 @@ __device__ __forceinline__ void prefill_rank(PrefillRank& rk, const int32_t* __r
 
 // Item w of the longest-first order as (chunk, row tile, kv head); false past the last item.
 // Every thread of the workgroup calls this (it synchronises).
-template <int G>
+template <int G, int TileRows = kTileRows>
 __device__ __forceinline__ bool prefill_locate(PrefillRank& rk, int w,
                                                const int32_t* __restrict__ query_start_loc,
                                                int num_chunks, int num_kv_heads, int& c,
@@ -88,15 +122,15 @@ __device__ __forceinline__ bool prefill_locate(PrefillRank& rk, int w,
   __syncthreads();                  // item[] is rewritten by the next call
   if (c < 0) return false;
   const int n = query_start_loc[c + 1] - query_start_loc[c];
-  const int tiles = (n * G + kTileRows - 1) / kTileRows;
+  const int tiles = (n * G + TileRows - 1) / TileRows;
   tile = tiles - 1 - local / num_kv_heads;
   kvh = local % num_kv_heads;
   return true;
 }
 
-// One work item (chunk c, row tile, kv head) with all kThreads threads of the workgroup; the
-// eight arrays are the 4-stage K/V ring, each kKvTile x kChunks 16-byte chunks.
-template <int G>
+// One work item (chunk c, row tile, kv head) with all PfShape<D>::kThreads threads of the
+// workgroup; the eight arrays are the 4-stage K/V ring, each kKvTile x kChunks 16-byte chunks.
+template <int G, int D = kTileD>
 __device__ __forceinline__ void prefill_item(
     bf16_t* __restrict__ out, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -104,7 +138,13 @@ __device__ __forceinline__ void prefill_item(
     int num_kv_heads, int max_blocks_per_seq, float scale_log2, int c, int tile, int kvh,
     uint4* sK0, uint4* sK1, uint4* sK2, uint4* sK3, uint4* sV0, uint4* sV1, uint4* sV2,
     uint4* sV3) {
-  constexpr int kTokPerTile = kTileRows / G;
+  using Sh = PfShape<D>;
+  constexpr int kD = Sh::kD;
+  constexpr int kChunks = Sh::kChunks;
+  constexpr int kRowBytes = Sh::kRowBytes;
+  constexpr int kKvTile = Sh::kKvTile;
+  constexpr int kTokPerTile = Sh::kTileRows / G;
+  constexpr int kWaitTile = wait_vmcnt(Sh::kLoads);   // one tile's loads still in flight
   const int tid = threadIdx.x;
   const int q0 = query_start_loc[c];
   const int n = query_start_loc[c + 1] - q0;
@@ -148,11 +188,12 @@ __device__ __forceinline__ void prefill_item(
   // exactly the block's valid rows, so rows past the sequence end (and blocks past it, whose
   // table entry is not read) come in as zeros.  In load j lane l writes LDS chunk
   // (16*blk + 4j + l/16, l%16) and so fetches the logical chunk whose swizzled position that is.
-  const int stage_blk = wave % 4;
-  const bool stage_v = wave >= 4;
+  const int stage_blk = wave % (Sh::kWaves / 2);
+  const bool stage_v = wave >= Sh::kWaves / 2;
   const bf16_t* stage_pool = stage_v ? v_cache : k_cache;
   auto load_tile = [&](int kt, uint4* kdst, uint4* vdst) {
-    const int lb = wave_uniform(kt * 4 + stage_blk);   // keeps the table read a scalar load
+    // uniform, so the table read is a scalar load
+    const int lb = wave_uniform(kt * (kKvTile / kBlock) + stage_blk);
     const int first = lb * kBlock;
     const int rows = max(0, min(kBlock, L - first));
     const int phys = lb < nblk ? wave_uniform(table[lb]) : 0;
@@ -168,12 +209,12 @@ __device__ __forceinline__ void prefill_item(
         reinterpret_cast<bf16_t*>(su), 0, wave_uniform(rows * kRowBytes), kRsrcWord3);
     uint4* dst = (stage_v ? vdst : kdst) + stage_blk * kBlock * kChunks;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int slot = 4 * j + lane / 16;
+    for (int j = 0; j < Sh::kLoads; ++j) {
+      const int slot = Sh::kKeysPerLoad * j + lane / kChunks;
       const int key = stage_blk * kBlock + slot;
-      const int pchunk = lane % 16;
-      const int lchunk = stage_v ? v_swz(key, pchunk) : k_swz(key, pchunk);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + 4 * j * kChunks), 16,
+      const int pchunk = lane % kChunks;
+      const int lchunk = stage_v ? Sh::vswz(key, pchunk) : Sh::kswz(key, pchunk);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + j * kWave), 16,
                                                slot * kRowBytes + lchunk * 16, 0, 0, 0);
     }
   };
@@ -189,25 +230,25 @@ __device__ __forceinline__ void prefill_item(
 
   // S^T = K Q^T for one 64-key tile.  Operands are read half the head dim at a time, and the
   // two key subtiles' MFMAs alternate so back-to-back MFMAs never depend on each other.
-  auto qk = [&](const uint4* kbuf, f32x16_t (&sacc)[2]) {
+  auto qk = [&](const uint4* kbuf, f32x16_t (&sacc)[Sh::kKeySub]) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < Sh::kKeySub; ++t2)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[t2][v] = 0.f;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      uint4 a[2][4];
+    for (int kh = 0; kh < kD / 64; ++kh) {
+      uint4 a[Sh::kKeySub][4];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
+      for (int t2 = 0; t2 < Sh::kKeySub; ++t2) {
         const int key = t2 * 32 + col;
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4)
-          a[t2][k4] = kbuf[key * kChunks + k_swz(key, (kh * 4 + k4) * 2 + half)];
+          a[t2][k4] = kbuf[key * kChunks + Sh::kswz(key, (kh * 4 + k4) * 2 + half)];
       }
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+        for (int t2 = 0; t2 < Sh::kKeySub; ++t2)
           sacc[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               as_bf16x8(a[t2][k4]), as_bf16x8(qreg[kh * 4 + k4]), sacc[t2], 0, 0, 0);
     }
@@ -219,7 +260,7 @@ __device__ __forceinline__ void prefill_item(
   //   only tile kt+3 is still in flight (tile kt+2 is what the next step reads) and publish.
   // Tile t lives in stage t % 4.  A request past the last tile loads only zeros.
   auto step = [&](int kt, const uint4* knext, const uint4* vcur, uint4* kload, uint4* vload,
-                  f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+                  f32x16_t (&cur)[Sh::kKeySub], f32x16_t (&nxt)[Sh::kKeySub]) {
     load_tile(kt + 3, kload, vload);
 
     if (kt * kKvTile < kv_end_w) {
@@ -233,7 +274,7 @@ __device__ __forceinline__ void prefill_item(
       const bool need_mask = kt * kKvTile + kKvTile - 1 > prefix + t_lo_w;
       if (need_mask) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+        for (int t2 = 0; t2 < Sh::kKeySub; ++t2)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = kt * kKvTile + t2 * 32 + (v / 4) * 8 + half * 4 + (v % 4);
@@ -242,7 +283,7 @@ __device__ __forceinline__ void prefill_item(
       }
       float mx = cur[0][0];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < Sh::kKeySub; ++t2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, cur[t2][v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -262,7 +303,7 @@ __device__ __forceinline__ void prefill_item(
       const float mc = m_run * scale_log2;
       float psum = 0.f;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < Sh::kKeySub; ++t2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = fast_exp2(fmaf(cur[t2][v], scale_log2, -mc));
@@ -272,9 +313,9 @@ __device__ __forceinline__ void prefill_item(
       l_run += psum;
 
       // P^T operand for k-step s: the lane's own scores v = (s%2)*8 .. +8 of key subtile s/2
-      uint4 pT[4];
+      uint4 pT[Sh::kPvSteps];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < Sh::kPvSteps; ++s) {
         const f32x16_t& p = cur[s / 2];
         const int o = (s % 2) * 8;
         pT[s] = make_uint4(pack_bf16x2(p[o + 0], p[o + 1]), pack_bf16x2(p[o + 2], p[o + 3]),
@@ -289,7 +330,7 @@ __device__ __forceinline__ void prefill_item(
       const int g = lane / 16;
       const int jj = lane % 16;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < Sh::kPvSteps; ++s) {
         uint4 a[kD / 32];
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt) {
@@ -299,7 +340,7 @@ __device__ __forceinline__ void prefill_item(
           for (int sub = 0; sub < 2; ++sub) {
             const int key = 16 * s + 8 * sub + 4 * half + jj / 4;
             const char* rowp = reinterpret_cast<const char*>(vcur + key * kChunks);
-            part[sub] = lds_read_tr16(rowp + v_swz(key, unit >> 1) * 16 + (unit & 1) * 8);
+            part[sub] = lds_read_tr16(rowp + Sh::vswz(key, unit >> 1) * 16 + (unit & 1) * 8);
           }
           a[dt] = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
         }
@@ -310,10 +351,10 @@ __device__ __forceinline__ void prefill_item(
       }
     }
 
-    // every wave issued exactly four loads per step: the newest four (tile kt+3) may stay
-    // in flight, everything older (tile kt+2, read next step) must have landed.  A bare
+    // every wave issued exactly kLoads loads per step: the newest (tile kt+3) may stay in
+    // flight, everything older (tile kt+2, read next step) must have landed.  A bare
     // s_barrier, not __syncthreads: its memory fence would wait for the prefetch as well.
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_waitcnt(kWaitTile);
     __builtin_amdgcn_s_barrier();
   };
 
@@ -321,9 +362,9 @@ __device__ __forceinline__ void prefill_item(
   load_tile(0, sK0, sV0);
   load_tile(1, sK1, sV1);
   load_tile(2, sK2, sV2);
-  __builtin_amdgcn_s_waitcnt(kWaitVm4);
+  __builtin_amdgcn_s_waitcnt(kWaitTile);
   __builtin_amdgcn_s_barrier();
-  f32x16_t sa[2], sb[2];
+  f32x16_t sa[Sh::kKeySub], sb[Sh::kKeySub];
   qk(sK0, sa);
   for (int kt = 0; kt < num_kv_tiles; kt += 4) {
     step(kt, sK1, sV0, sK3, sV3, sa, sb);

@@ -143,7 +143,7 @@ def _grouped(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(gs=None), INV), (dict(sb=None), INV), (dict(NG=0), INV), (dict(NG=17), INV),
     (dict(MG=17), INV), (dict(MG=0), INV), (dict(Hq=30), INV), (dict(maxlen=300 * 16 + 1), INV),
-    (dict(scale=0.0), INV), (dict(ws=P + 4), INV), (dict(dtype=0), UNS), (dict(D=64), UNS),
+    (dict(scale=0.0), INV), (dict(ws=P + 4), INV), (dict(dtype=0), UNS), (dict(D=96), UNS),
     (dict(B=32, MB=150), UNS), (dict(Hq=128), UNS), (dict(wsb=64), WS), (dict(ws=None), WS),
 ])
 def test_grouped_decode_rejects(kw, status):
@@ -221,7 +221,7 @@ def _prefill(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(qsl=None), INV), (dict(C=0), INV), (dict(Hq=30), INV), (dict(maxq=5000), INV),
-    (dict(maxlen=600 * 16 + 1), INV), (dict(dtype=0), UNS), (dict(D=64), UNS),
+    (dict(maxlen=600 * 16 + 1), INV), (dict(dtype=0), UNS), (dict(D=96), UNS),
     (dict(scale=-1.0), INV),
     (dict(Hq=128, Hkv=8), UNS),
 ])

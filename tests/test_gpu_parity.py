@@ -406,10 +406,10 @@ def test_prefill_ragged_chunks(G):
     assert_close(widen(out), want, ATOL, RTOL, f"prefill G{G}")
 
 
-def _prefill_case(seed, chunk_lens, prefixes, G, num_kv_heads=2):
+def _prefill_case(seed, chunk_lens, prefixes, G, num_kv_heads=2, head_dim=128):
     m = W.mixed_bf16(device=DEV, num_chunks=len(chunk_lens), chunk_len=0, num_decode=1,
                      median=20, cap=40, num_q_heads=G * num_kv_heads,
-                     num_kv_heads=num_kv_heads, head_dim=128, seed=seed,
+                     num_kv_heads=num_kv_heads, head_dim=head_dim, seed=seed,
                      chunk_lens=list(chunk_lens), prefixes=list(prefixes))
     run_append(m.k_cache, m.v_cache, m.k_new, m.v_new, m.slot_mapping)
     out = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
@@ -438,6 +438,42 @@ def test_prefill_short_and_tied_chunks():
     again = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
                         m.query_start_loc, m.scale)
     assert torch.equal(again, out), "prefill reruns differ"
+
+
+@pytest.mark.parametrize("D,G", [(64, 1), (64, 4), (64, 8), (256, 1), (256, 2), (256, 4),
+                                 (256, 8)])
+def test_prefill_head_dims(D, G):
+    """head_dim 64 (64-key tiles of half-width rows) and 256 (128-row work items of four waves,
+    32-key tiles): ragged chunks over ragged prefixes, several row tiles per chunk, a prefix-0
+    chunk and a one-row chunk."""
+    say(f"case: prefill head_dim {D}, G={G}")
+    _, out, want = _prefill_case(1510 + D + G, [1, 77, 300, 128, 33, 257],
+                                 [0, 5, 700, 64, 129, 1000], G, head_dim=D)
+    assert_close(widen(out), want, ATOL, RTOL, f"prefill D{D} G{G}")
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_prefill_head_dims_long_prefix(D):
+    """Chunks over 65k and 20k prefixes: hundreds of key tiles through the 4-stage ring."""
+    say(f"case: prefill head_dim {D} over 65k and 20k prefixes")
+    _, out, want = _prefill_case(1540 + D, [200, 31], [65000, 20011], G=4, head_dim=D)
+    assert_close(widen(out), want, ATOL, RTOL, f"prefill D{D} long prefix")
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_prefill_head_dims_short_tied_and_many(D):
+    """Short and tied chunks (ranked path, reruns identical), then 131 chunks (in-order path)."""
+    say(f"case: prefill head_dim {D}, short/tied chunks, then 131 chunks")
+    m, out, want = _prefill_case(1520 + D, [1, 3, 64, 64, 64, 17, 130],
+                                 [0, 10, 100, 100, 100, 0, 0], G=8, head_dim=D)
+    assert_close(widen(out), want, ATOL, RTOL, f"prefill D{D} short/tied")
+    again = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
+                        m.query_start_loc, m.scale)
+    assert torch.equal(again, out), "prefill reruns differ"
+    rng = np.random.default_rng(1530 + D)
+    _, out, want = _prefill_case(1531 + D, rng.integers(1, 40, size=131),
+                                 rng.integers(0, 200, size=131), G=4, head_dim=D)
+    assert_close(widen(out), want, ATOL, RTOL, f"prefill D{D} 131 chunks")
 
 
 def test_prefill_one_row_chunk_equals_decode():
