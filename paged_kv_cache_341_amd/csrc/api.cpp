@@ -60,9 +60,10 @@ bool decode_block_supported(int b) {
   return b == 1 || b == 4 || b == 8 || b == 16 || b == 32 || b == 64;
 }
 
-// Tokens per unit of the decode split walk: the block size, or 16 for blocks smaller than 8
-// (their tokens are looked up one by one) and for contiguous KV (block_size 0 here).
-int decode_unit(int block_size) { return block_size >= 8 ? block_size : 16; }
+// Tokens per unit of the decode split walk: the block size for 8- and 16-token blocks, else 16:
+// blocks smaller than 8 tokens are looked up token by token, blocks larger than 16 are walked
+// 16 tokens at a time, and contiguous KV (block_size 0 here) as 16-token blocks.
+int decode_unit(int block_size) { return block_size == 8 || block_size == 16 ? block_size : 16; }
 
 // Tokens per unit of the contiguous decode (the same walk as 16-token paged blocks).
 constexpr int kContiguousUnit = 16;

@@ -67,6 +67,37 @@ struct PagedRows {
   }
 };
 
+// Paged, blocks of BT > U tokens (a block holds BT/U units): unit u is run u % (BT/U) of U rows
+// of physical block table[u / (BT/U)].  The walk, its load batches and the split plan are then
+// those of U-token blocks, so a split's four waves share its units evenly however large the
+// blocks are.  prepare() reads one table entry per unit (neighbouring units repeat an entry).
+template <typename T, int D, int U, int BT>
+struct PagedLargeRows {
+  static_assert(BT > U && BT % U == 0, "large blocks must hold whole units");
+  static constexpr int kPer = BT / U;
+  const int32_t* table;
+  int num_kv_heads, kvh;
+  int first = 0, stride = 1;
+  // lane l: for unit v = first + l * stride (lanes < count), the index of its U-row run in the
+  // pool counted for kv head 0: table[v / kPer] * num_kv_heads * kPer + v % kPer.  The run of
+  // kv head h is that plus h * kPer.
+  int runs = 0;
+  __device__ __forceinline__ void prepare(int first_unit, int count, int stride_units) {
+    first = first_unit;
+    stride = stride_units;
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const unsigned v = static_cast<unsigned>(first + lane * stride);
+    runs = lane < count ? table[v / kPer] * num_kv_heads * kPer + static_cast<int>(v % kPer) : 0;
+  }
+  __device__ __forceinline__ const T* unit(const T* cache, int u) const {
+    const int run = __builtin_amdgcn_readlane(runs, wave_uniform((u - first) / stride));
+    return cache + (static_cast<size_t>(run) + kvh * kPer) * (static_cast<size_t>(U) * D);
+  }
+  __device__ __forceinline__ const T* row(const T*, const T* base, int, int k) const {
+    return base + static_cast<size_t>(k) * D;
+  }
+};
+
 // Paged, blocks of BT < U tokens (a unit spans U/BT blocks): every lane looks up the block of
 // the token it loads.  Tokens past the sequence end (the tail of its last unit) are read from
 // its last token instead, so no table entry past ceil(len/BT) is touched; they are masked out

@@ -31,8 +31,8 @@
 namespace pa {
 
 // U: tokens per unit of the split walk (the pool's block size when BT == U); BT: tokens per
-// pool block (BT < U: blocks smaller than a unit, looked up per token); Contig: no table, the
-// cache is [num_seqs][num_kv_heads][capacity][D].
+// pool block (BT < U: blocks smaller than a unit, looked up per token; BT > U: blocks holding
+// several units); Contig: no table, the cache is [num_seqs][num_kv_heads][capacity][D].
 template <typename T, int D, int G, int U, int BT, bool Contig>
 __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
     T* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
@@ -65,6 +65,13 @@ __global__ __launch_bounds__(kDecodeThreads) void pa_decode_split_kernel(
   } else if constexpr (BT == U) {
     const PagedRows<T, D, U> rows{block_tables + static_cast<size_t>(s) * max_blocks_per_seq,
                                   num_kv_heads, kvh};
+    decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
+        out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
+        plan, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
+        stat_l, late);
+  } else if constexpr (BT > U) {
+    const PagedLargeRows<T, D, U, BT> rows{
+        block_tables + static_cast<size_t>(s) * max_blocks_per_seq, num_kv_heads, kvh};
     decode_split_item<T, D, G, U, kDecodeWaves, 0, true>(
         out, ws_ml, ws_acc, q, k_cache, v_cache, rows, L, skip_blocks, slot_base, num_kv_heads,
         plan, nsplit_max, scale_log2, s, kvh, static_cast<int>(blockIdx.y), smem, red, stat_m,
@@ -262,8 +269,8 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
     case 4: return launch_decode_tb<T, D, G, 16, 4, false>(a);
     case 8: return launch_decode_tb<T, D, G, 8, 8, false>(a);
     case 16: return launch_decode_tb<T, D, G, 16, 16, false>(a);
-    case 32: return launch_decode_tb<T, D, G, 32, 32, false>(a);
-    case 64: return launch_decode_tb<T, D, G, 64, 64, false>(a);
+    case 32: return launch_decode_tb<T, D, G, 16, 32, false>(a);
+    case 64: return launch_decode_tb<T, D, G, 16, 64, false>(a);
   }
   return hipErrorInvalidValue;
 }

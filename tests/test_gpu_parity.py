@@ -104,7 +104,8 @@ def _shrinking_plan_slots(max_len, G, unit):
 
 @pytest.mark.parametrize("G,D,dtype,B", [(1, 64, "bf16", 16), (2, 256, "bf16", 16),
                                          (8, 128, "bf16", 16), (2, 128, "f32", 32),
-                                         (4, 128, "bf16", 8), (4, 64, "bf16", 1)])
+                                         (4, 128, "bf16", 8), (4, 64, "bf16", 1),
+                                         (4, 128, "bf16", 64)])
 def test_decode_shrinking_split_plans(G, D, dtype, B):
     """64 sequences x 8 kv heads of up to 4096 tokens take split sizes that shrink toward the
     last splits (checked through the workspace size); every row against the oracle, with
@@ -115,7 +116,7 @@ def test_decode_shrinking_split_plans(G, D, dtype, B):
     lens = edges + rng.integers(1, 4097, size=64 - len(edges)).tolist()
     b = W.make_decode(lens, 8 * G, 8, D, dtype, seed=2600 + G + D + B, device=DEV,
                       block_size=B)
-    unit = B if B >= 8 else 16
+    unit = B if B in (8, 16) else 16
     size = ops.pa_decode_workspace_size(64, 8 * G, 8, D, B, 4096)
     assert split_slots(size, 64 * 8 * G, D) == _shrinking_plan_slots(4096, G, unit)
     out = run_decode(b)
@@ -169,11 +170,12 @@ def test_decode_needle(jstar):
     assert np.max(np.abs(widen(out)[0, 0] - target)) < 0.05
 
 
-@pytest.mark.parametrize("B", [1, 4])
-@pytest.mark.parametrize("jstar", [0, 3, 4, 15, 16, 2999])
-def test_decode_small_block_needle(B, jstar):
-    """Needles at block and 16-token unit edges with blocks smaller than a unit (each token's
-    block is looked up on its own)."""
+@pytest.mark.parametrize("B", [1, 4, 32, 64])
+@pytest.mark.parametrize("jstar", [0, 3, 4, 15, 16, 31, 32, 63, 64, 2999])
+def test_decode_block_size_needle(B, jstar):
+    """Needles at block and 16-token unit edges, with blocks smaller than a unit (each token's
+    block is looked up on its own) and larger than one (a block is walked 16 tokens at a
+    time)."""
     L = 3000
     say(f"case: needle at {jstar} of {L}, block size {B}")
     b = W.make_decode([L, 77], 4, 1, 128, "bf16", seed=710 + B, device=DEV, block_size=B)
@@ -181,7 +183,7 @@ def test_decode_small_block_needle(B, jstar):
     qv = b.q[0, 0].float()
     b.k_cache[phys, 0, jstar % B] = (qv * (40.0 / (b.scale * float(qv @ qv)))).to(torch.bfloat16)
     out = run_decode(b)
-    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, "small-block needle")
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, f"block size {B} needle")
     target = b.v_cache[phys, 0, jstar % B].float().cpu().numpy()
     assert np.max(np.abs(widen(out)[0, 0] - target)) < 0.05
 
