@@ -11,7 +11,7 @@ while a 30,000-token prompt arrives) with and without a per-step token cap, each
 events on the stream the kernels run on.  Inputs are synthetic and already resident in HBM when
 timing starts.
 
-`--gpus N` with N > 1 is refused: this build runs on one GPU.
+`--gpus N` with N > 1 is refused: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 

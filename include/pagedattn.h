@@ -58,7 +58,7 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, misalignment, bad ratio */
-  PA_ERR_UNSUPPORTED = 2,        /* a valid request this build has no kernel for */
+  PA_ERR_UNSUPPORTED = 2,        /* a valid request the library has no kernel for */
   PA_ERR_WORKSPACE_TOO_SMALL = 3,
   PA_ERR_DEVICE = 4              /* the HIP runtime reported an error at launch */
 } pa_status;
