@@ -266,7 +266,7 @@ pa_status cow_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pai
  * no initialisation; the call uses its first 256 bytes as work counters and the rest as the
  * decode split partials.
  *
- * Supported: dtype BF16, head_dim 128, block_size 16, num_q_heads/num_kv_heads in
+ * Supported: dtype BF16, head_dim 64, 128 or 256, block_size 16, num_q_heads/num_kv_heads in
  * {1, 2, 4, 8}, at most 128 chunks and 2048 decode sequences.  Device-content preconditions
  * are those of the three calls it replaces.
  */

@@ -543,8 +543,8 @@ MixedPlan plan_mixed(int num_seqs, int num_q_heads, int num_kv_heads, int head_d
 
 size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int32_t dec_max_seq_len) {
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != 128 ||
-      block_size != kSupportedBlock || num_q_heads % num_kv_heads != 0 ||
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      (head_dim != 64 && head_dim != 128 && head_dim != 256) || block_size != kSupportedBlock || num_q_heads % num_kv_heads != 0 ||
       (num_seqs > 0 && dec_max_seq_len <= 0))
     return 0;
   return plan_mixed(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, dec_max_seq_len)
@@ -591,9 +591,10 @@ pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspa
   }
   if (b->dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: only bf16 is supported");
-  if (b->head_dim != 128 || b->block_size != kSupportedBlock)
+  if ((b->head_dim != 64 && b->head_dim != 128 && b->head_dim != 256) ||
+      b->block_size != kSupportedBlock)
     return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: head_dim %d, block_size %d (supported: "
-                "128, 16)", b->head_dim, b->block_size);
+                "64, 128 or 256; 16)", b->head_dim, b->block_size);
   const int g = b->num_q_heads / b->num_kv_heads;
   if (!supported_group(g))
     return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: %d query heads per kv head (supported: "
@@ -680,6 +681,7 @@ pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspa
   m.v_cache = b->v_cache;
   m.num_q_heads = b->num_q_heads;
   m.num_kv_heads = b->num_kv_heads;
+  m.head_dim = b->head_dim;
   m.num_workgroups = cus;
   m.scale_log2 = b->scale * 1.4426950408889634f;
   m.stream = st;

@@ -114,7 +114,7 @@ struct MixedArgs {
   // shared
   const void* k_cache;
   const void* v_cache;
-  int num_q_heads, num_kv_heads, num_workgroups;
+  int num_q_heads, num_kv_heads, head_dim, num_workgroups;
   float scale_log2;
   hipStream_t stream;
 };

@@ -249,16 +249,26 @@ hipError_t launch_decode_tb(const DecodeArgs& a) {
   return hipGetLastError();
 }
 
-// The merge for the partials of bf16, D 128, B 16 splits written by another kernel.
-hipError_t launch_decode_merge(const DecodeArgs& a) {
-  if (a.nsplit_max <= 1) return hipSuccess;
+// The merge for the partials of bf16, 16-token-unit splits written by another kernel.
+template <int D>
+static hipError_t launch_decode_merge_d(const DecodeArgs& a) {
   const int rows = a.num_seqs * a.num_q_heads;
-  hipLaunchKernelGGL((pa_decode_merge_kernel<bf16_t, 128, 16>),
+  hipLaunchKernelGGL((pa_decode_merge_kernel<bf16_t, D, 16>),
                      dim3((rows + kMergeWaves - 1) / kMergeWaves), dim3(kMergeWaves * kWave), 0,
                      a.stream, static_cast<bf16_t*>(a.out), a.ws_ml, a.ws_acc, a.seq_lens,
                      a.skip_blocks, a.slot_base, a.shared_split_keys, rows, a.num_q_heads,
                      a.plan, a.nsplit_max);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a) {
+  if (a.nsplit_max <= 1) return hipSuccess;
+  switch (a.head_dim) {
+    case 64: return launch_decode_merge_d<64>(a);
+    case 128: return launch_decode_merge_d<128>(a);
+    case 256: return launch_decode_merge_d<256>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D, int G>

@@ -9,8 +9,8 @@
 // different units: the chunks by the matrix cores, the decodes by HBM.  Run back to back, each
 // leaves the other's unit idle; here they share the chip at the same time.
 //
-// Design (ours): one workgroup of 8 waves per CU (the prefill item's shape: 256 rows, the
-// 4-stage K/V ring in LDS).  Two work queues, each an atomic counter in the workspace that the
+// Design (ours): one workgroup per CU in the prefill item's shape for the head dim (8 waves and
+// 256 rows at head_dim 64 and 128, 4 waves and 128 rows at 256; the 4-stage K/V ring in LDS).  Two work queues, each an atomic counter in the workspace that the
 // append launch before this one zeroes:
 //   * prefill items (chunk, row tile, kv head), longest chunk first (ranked in LDS from
 //     seq_lens, as in the prefill kernel);
@@ -31,7 +31,6 @@ namespace pa {
 namespace {
 
 constexpr int kMixedSeqCap = 2048;        // decode sequences enumerated in LDS
-constexpr int kRing = kKvTile * kChunks;  // uint4 per K or V ring stage
 // Blocks a decode wave loads together.  The prefill path fixes the register budget (256), so
 // deeper batches than the standalone decode's would cost no occupancy, but measured on the
 // mixed iteration they were slower (8 and 12 blocks against 4): at two waves per SIMD a wave
@@ -40,8 +39,8 @@ constexpr int kMixedDecodeBatch = 0;      // the standalone decode's 64 tokens
 
 }  // namespace
 
-template <int G>
-__global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
+template <int G, int D>
+__global__ __launch_bounds__(PfShape<D>::kThreads, 1) void pa_mixed_kernel(
     bf16_t* __restrict__ chunk_out, const bf16_t* __restrict__ chunk_q,
     const int32_t* __restrict__ chunk_tables, const int32_t* __restrict__ chunk_seq_lens,
     const int32_t* __restrict__ query_start_loc, int num_chunks, int chunk_max_blocks,
@@ -50,11 +49,19 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
     int num_seqs, int dec_max_blocks, int bps, int nsplit_max, float* __restrict__ ws_ml,
     float* __restrict__ ws_acc, int* __restrict__ queues, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, int num_kv_heads, float scale_log2) {
-  // the prefill ring; a decode item uses the same memory for its scores and partial sums
+  // the prefill ring; a decode item uses the same memory for its scores and partial sums (at
+  // most 8192 scores, the split planner's cap, and Waves x G x D partial sums: 32 KiB, within
+  // the smallest ring)
+  using Sh = PfShape<D>;
+  constexpr int kThr = Sh::kThreads;
+  constexpr int kRing = Sh::kRing;
+  static_assert(kThr >= kRankCap && kMixedSeqCap % kThr == 0, "workgroup shape");
+  static_assert(8 * kRing * 16 >= 8192 * 4 && 8 * kRing * 16 >= Sh::kWaves * 8 * D * 4,
+                "the ring holds a decode item's scores and partial sums");
   __shared__ uint4 ring[8 * kRing];
   __shared__ PrefillRank rk;
   __shared__ int dscan[kMixedSeqCap];
-  __shared__ float dred[kWaves][G];
+  __shared__ float dred[Sh::kWaves][G];
   __shared__ float dstat_m[G];
   __shared__ float dstat_l[G];
   __shared__ int s_ticket[2];
@@ -62,11 +69,11 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
   const int tid = threadIdx.x;
 
   // ------------------------------------------------------------ the two work lists
-  prefill_rank<G>(rk, chunk_seq_lens, query_start_loc, num_chunks, num_kv_heads);
+  prefill_rank<G, Sh::kTileRows>(rk, chunk_seq_lens, query_start_loc, num_chunks, num_kv_heads);
   const int total_prefill = num_chunks > 0 ? rk.scan[num_chunks - 1] : 0;
   // splits per sequence, then an inclusive scan over sequences (blocked: each thread scans a
   // run of consecutive sequences, then the run totals are scanned)
-  constexpr int kPer = kMixedSeqCap / kThreads;
+  constexpr int kPer = kMixedSeqCap / kThr;
   {
     int run[kPer];
     int acc = 0;
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
     reinterpret_cast<int*>(ring)[tid] = acc;     // run totals, scanned in place
     __syncthreads();
     int* tot = reinterpret_cast<int*>(ring);
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < kThr; off <<= 1) {
       const int v = tid >= off ? tot[tid - off] : 0;
       __syncthreads();
       tot[tid] += v;
@@ -123,8 +130,9 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
     if (which < 0) break;                          // both queues are empty
     if (which == 0) {
       int c, tile, kvh;
-      if (prefill_locate<G>(rk, t, query_start_loc, num_chunks, num_kv_heads, c, tile, kvh))
-        prefill_item<G>(chunk_out, chunk_q, k_cache, v_cache, chunk_tables, chunk_seq_lens,
+      if (prefill_locate<G, Sh::kTileRows>(rk, t, query_start_loc, num_chunks, num_kv_heads, c,
+                                           tile, kvh))
+        prefill_item<G, D>(chunk_out, chunk_q, k_cache, v_cache, chunk_tables, chunk_seq_lens,
                         query_start_loc, num_kv_heads, chunk_max_blocks, scale_log2, c, tile,
                         kvh, ring + 0 * kRing, ring + 1 * kRing, ring + 2 * kRing,
                         ring + 3 * kRing, ring + 4 * kRing, ring + 5 * kRing, ring + 6 * kRing,
@@ -139,9 +147,9 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
       }
       const int s = wave_uniform(lo);
       const int split = j - (s > 0 ? dscan[s - 1] : 0);
-      const PagedRows<bf16_t, kD, kBlock> rows{
+      const PagedRows<bf16_t, D, kBlock> rows{
           dec_tables + static_cast<size_t>(s) * dec_max_blocks, num_kv_heads, kvh};
-      decode_split_item<bf16_t, kD, G, kBlock, kWaves, kMixedDecodeBatch>(
+      decode_split_item<bf16_t, D, G, kBlock, Sh::kWaves, kMixedDecodeBatch>(
           dec_out, ws_ml, ws_acc, dec_q, k_cache, v_cache, rows, dec_seq_lens[s], nullptr, 0,
           num_kv_heads, SplitPlan::uniform(bps), nsplit_max, scale_log2, s, kvh, split,
           reinterpret_cast<float*>(ring), dred, dstat_m, dstat_l);
@@ -150,9 +158,10 @@ __global__ __launch_bounds__(kThreads, 1) void pa_mixed_kernel(
   }
 }
 
-template <int G>
-static hipError_t launch_mixed_g(const MixedArgs& a) {
-  hipLaunchKernelGGL((pa_mixed_kernel<G>), dim3(a.num_workgroups), dim3(kThreads), 0, a.stream,
+template <int G, int D>
+static hipError_t launch_mixed_gd(const MixedArgs& a) {
+  hipLaunchKernelGGL((pa_mixed_kernel<G, D>), dim3(a.num_workgroups), dim3(PfShape<D>::kThreads),
+                     0, a.stream,
                      static_cast<bf16_t*>(a.chunk_out), static_cast<const bf16_t*>(a.chunk_q),
                      a.chunk_tables, a.chunk_seq_lens, a.query_start_loc, a.num_chunks,
                      a.chunk_max_blocks_per_seq, static_cast<bf16_t*>(a.dec_out),
@@ -161,6 +170,16 @@ static hipError_t launch_mixed_g(const MixedArgs& a) {
                      a.ws_acc, a.queues, static_cast<const bf16_t*>(a.k_cache),
                      static_cast<const bf16_t*>(a.v_cache), a.num_kv_heads, a.scale_log2);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_mixed_g(const MixedArgs& a) {
+  switch (a.head_dim) {
+    case 64: return launch_mixed_gd<G, 64>(a);
+    case 128: return launch_mixed_gd<G, 128>(a);
+    case 256: return launch_mixed_gd<G, 256>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_mixed(const MixedArgs& a) {

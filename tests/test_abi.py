@@ -165,7 +165,7 @@ def test_grouped_workspace_size():
     (dict(num_chunks=2, chunk_total_q=10, chunk_max_q_len=20, chunk_max_seq_len=30,
           chunk_max_blocks_per_seq=4, chunk_out=P, chunk_q=P, chunk_tables=P,
           chunk_seq_lens=P, query_start_loc=P), INV),
-    (dict(dtype=0), UNS), (dict(head_dim=64), UNS), (dict(num_q_heads=128), UNS),
+    (dict(dtype=0), UNS), (dict(head_dim=96), UNS), (dict(num_q_heads=128), UNS),
     (dict(num_seqs=3000), UNS), (dict(_wsb=16), WS),
 ])
 def test_mixed_step_rejects(kw, status):
@@ -207,6 +207,8 @@ def test_mixed_batch_layout(tmp_path):
     assert got == want
     assert ops.pa_mixed_workspace_size(0, 32, 8, 128, 16, 0) == 256
     assert ops.pa_mixed_workspace_size(192, 32, 8, 128, 16, 16384) > 192 * 32 * 130 * 4
+    assert ops.pa_mixed_workspace_size(8, 16, 4, 256, 16, 4096) > 8 * 16 * 258 * 4
+    assert ops.pa_mixed_workspace_size(8, 16, 4, 96, 16, 4096) == 0
 
 
 def _prefill(**kw):

@@ -668,6 +668,31 @@ def test_mixed_step_single_launch_ragged(G):
     assert_close(widen(dout), want, ATOL, RTOL, "mixed decodes")
 
 
+@pytest.mark.parametrize("D,G", [(64, 1), (64, 8), (256, 2), (256, 4), (256, 8)])
+def test_mixed_step_single_launch_head_dims(D, G):
+    """pa_mixed_step at head_dim 64 (8-wave workgroups) and 256 (4-wave workgroups, 128-row
+    chunk tiles): pool bit-exact after the append, chunk rows bit-identical to pa_prefill_chunk
+    and within tolerance of the oracle, every decode row against the oracle."""
+    say(f"case: mixed step single launch, head_dim {D}, G={G}")
+    m = W.mixed_bf16(device=DEV, seed=2100 + D + G, num_chunks=4, chunk_lens=[1, 77, 300, 129],
+                     prefixes=[0, 700, 33, 2000], num_decode=24, cap=5000,
+                     num_q_heads=2 * G, num_kv_heads=2, head_dim=D)
+    bk, bv = raw(m.k_cache), raw(m.v_cache)
+    cout, dout = run_mixed_step(m)
+    wk, wv = ref.append_ref(bk, bv, raw(m.k_new), raw(m.v_new), m.slot_mapping)
+    kc, vc = raw(m.k_cache), raw(m.v_cache)
+    assert np.array_equal(kc, wk) and np.array_equal(vc, wv)
+    want = ref.prefill_ref(raw(m.q_chunk), kc, vc, m.chunk_tables, m.chunk_seq_lens,
+                           m.query_start_loc, m.scale, "bf16")
+    assert_close(widen(cout), want, ATOL, RTOL, f"mixed chunks D{D}")
+    alone = run_prefill(m.q_chunk, m.k_cache, m.v_cache, m.chunk_tables, m.chunk_seq_lens,
+                        m.query_start_loc, m.scale)
+    assert torch.equal(cout, alone)
+    want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, f"mixed decodes D{D}")
+
+
 def test_mixed_step_single_launch_full_size():
     """The full mixed iteration (8 x 512-row chunks, 192 decodes) in one pa_mixed_step call,
     twice with the same garbage-filled workspace (the counters are reset by the call): pool
