@@ -166,7 +166,7 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
  *   other arguments as pa_decode; workspace of pa_decode_grouped_workspace_size(...) bytes,
  *   contents need no initialisation
  *
- * Supported: dtype BF16, head_dim 128, block_size 16, num_q_heads/num_kv_heads in
+ * Supported: dtype BF16, head_dim 64, 128 or 256, block_size 16, num_q_heads/num_kv_heads in
  * {1, 2, 4, 8}.  Arguments that break the equalities above give wrong values, never an
  * access outside the buffers the other arguments describe.
  */

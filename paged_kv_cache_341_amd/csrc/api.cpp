@@ -420,8 +420,8 @@ pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_grouped: scale must be finite and positive");
   if (dtype != PA_DTYPE_BF16)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: only bf16 is supported");
-  if (head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: head_dim %d (supported: 128)",
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: head_dim %d (supported: 64, 128, 256)",
                 head_dim);
   if (block_size != kSupportedBlock)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode_grouped: block_size %d (supported: 16)",
@@ -468,6 +468,7 @@ pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const
   sp.num_groups = num_groups;
   sp.num_q_heads = num_q_heads;
   sp.num_kv_heads = num_kv_heads;
+  sp.head_dim = head_dim;
   sp.max_blocks_per_seq = max_blocks_per_seq;
   sp.row_tiles = row_tiles;
   sp.nsplit_shared = p.nsplit_shared;

@@ -144,7 +144,7 @@ struct SharedPrefixArgs {
   const int32_t* group_start;    // [num_groups + 1]
   const int32_t* shared_blocks;  // [num_seqs]
   const int32_t* seq_lens;       // [num_seqs]
-  int num_seqs, num_groups, num_q_heads, num_kv_heads, max_blocks_per_seq;
+  int num_seqs, num_groups, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq;
   int row_tiles, nsplit_shared, split_keys, slot_base, nsplit_max;
   float scale_log2;
   hipStream_t stream;

@@ -7,17 +7,29 @@
 
 namespace pa {
 
-constexpr int kTileD = 128;                 // head dim of the MFMA kernels
-constexpr int kTileChunks = kTileD / 8;     // 16-byte chunks per key row (bf16)
-constexpr int kTileRowBytes = kTileD * 2;   // 256
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw 32-bit buffer, gfx9 family
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Swizzles of the row-major LDS tiles, in 16-byte chunks of a 256-byte key row.  K rows are
-// read one chunk per lane down 32 keys, V rows eight keys at a time by the transposing load.
-__device__ __forceinline__ int k_swz(int key, int chunk) { return chunk ^ (key & 15); }
-__device__ __forceinline__ int v_swz(int key, int chunk) { return chunk ^ ((key & 3) << 2); }
+// Row-major tiles of bf16 K or V rows of head_dim D in LDS, in 16-byte chunks, filled a 16-row
+// block at a time by 1 KiB buffer-to-LDS loads (64 lanes x 16 bytes: kKeysPerLoad rows each).
+// K rows are read one chunk per lane down 32 keys and V rows four keys at a time by the
+// transposing load; the XOR swizzles spread both over the LDS banks.
+template <int D>
+struct KvTile {
+  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunkBits = kChunks == 8 ? 3 : kChunks == 16 ? 4 : 5;
+  static constexpr int kLoadsPerBlock = kBlock * kRowBytes / 1024;
+  static constexpr int kKeysPerLoad = kWave / kChunks;
+  static __device__ __forceinline__ int kswz(int key, int chunk) {
+    return chunk ^ (key & (kChunks - 1));
+  }
+  static __device__ __forceinline__ int vswz(int key, int chunk) {
+    return chunk ^ ((key & 3) << (kChunkBits - 2));
+  }
+};
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -66,9 +78,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4* p) {
 // high bits [15:14], expcnt [6:4] and lgkmcnt [11:8] left at their maxima).
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | (((n >> 4) & 3) << 14); }
 constexpr int kWaitVm0 = wait_vmcnt(0);
-constexpr int kWaitVm4 = wait_vmcnt(4);
-constexpr int kWaitVm8 = wait_vmcnt(8);
-static_assert(kWaitVm4 == 0x0F74 && wait_vmcnt(16) == 0x4F70, "s_waitcnt encoding");
+static_assert(wait_vmcnt(4) == 0x0F74 && wait_vmcnt(16) == 0x4F70, "s_waitcnt encoding");
 
 // Explicit waits that are also compiler memory barriers (no memory access moves across them),
 // for LDS tiles filled by buffer_to_lds16_untracked.

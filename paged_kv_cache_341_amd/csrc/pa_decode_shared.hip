@@ -27,12 +27,11 @@ namespace {
 
 constexpr int kSpRows = 32;                   // rows per wave (one MFMA tile)
 constexpr int kSpKeys = 32;                   // keys per LDS tile (two 16-token blocks)
-constexpr int kSpChunks = kTileChunks;
 constexpr float kSpLazyLog2 = 8.f;
 
 }  // namespace
 
-template <int G>
+template <int G, int D>
 __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
     float* __restrict__ ws_ml, float* __restrict__ ws_acc, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k_cache, const bf16_t* __restrict__ v_cache,
@@ -40,9 +39,14 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
     const int32_t* __restrict__ shared_blocks, const int32_t* __restrict__ seq_lens,
     int num_seqs, int num_kv_heads, int max_blocks_per_seq,
     int row_tiles, int split_keys, int slot_base, int nsplit_max, float scale_log2) {
-  constexpr int kD = kTileD;
-  __shared__ uint4 sK0[kSpKeys * kSpChunks], sK1[kSpKeys * kSpChunks];   // 2 x 8 KiB
-  __shared__ uint4 sV0[kSpKeys * kSpChunks], sV1[kSpKeys * kSpChunks];   // 2 x 8 KiB
+  using L = KvTile<D>;
+  constexpr int kD = D;
+  constexpr int kSpChunks = L::kChunks;
+  // loads per tile: two blocks of K and V; the counted waits keep one tile's loads in flight
+  constexpr int kTileLoads = 2 * 2 * L::kLoadsPerBlock;
+  // 2 x 8 KiB each at head_dim 128 (4 KiB at 64, 16 KiB at 256)
+  __shared__ uint4 sK0[kSpKeys * kSpChunks], sK1[kSpKeys * kSpChunks];
+  __shared__ uint4 sV0[kSpKeys * kSpChunks], sV1[kSpKeys * kSpChunks];
 
   const int item = blockIdx.x;
   const int kvh = item % num_kv_heads;
@@ -92,8 +96,9 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // Tile t holds keys k_begin + 32t .. +31: two blocks.  Each block's descriptors cover only
-  // its keys below k_end, so keys past the split's end arrive as zeros; all 16 loads are
-  // always issued.  In load j of block bi lane l writes LDS chunk (16 bi + 4 j + l/16, l%16).
+  // its keys below k_end, so keys past the split's end arrive as zeros; all kTileLoads loads
+  // are always issued.  In load j of block bi lane l writes LDS row 16 bi + kKeysPerLoad j +
+  // l / kChunks, chunk l % kChunks.
   auto load_tile = [&](int t, const uint4* kdst, const uint4* vdst) {
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
@@ -103,17 +108,18 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
       const int rows = wave_uniform(max(0, min(kBlock, k_end - k_begin - lblk * kBlock)));
       const int phys = rows > 0 ? __builtin_amdgcn_readlane(my_block, lblk) : 0;
       const size_t off = (static_cast<size_t>(phys) * num_kv_heads + kvh) * slab;
-      const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k_cache + off, rows * kTileRowBytes);
-      const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v_cache + off, rows * kTileRowBytes);
+      const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(k_cache + off, rows * L::kRowBytes);
+      const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(v_cache + off, rows * L::kRowBytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int slot = 4 * j + lane / 16;
+      for (int j = 0; j < L::kLoadsPerBlock; ++j) {
+        const int slot = L::kKeysPerLoad * j + lane / kSpChunks;
         const int key = bi * kBlock + slot;
-        const int pchunk = lane % 16;
-        buffer_to_lds16_untracked(krs, lds_addr(kdst + (bi * kBlock + 4 * j) * kSpChunks),
-                                  slot * kTileRowBytes + k_swz(key, pchunk) * 16);
-        buffer_to_lds16_untracked(vrs, lds_addr(vdst + (bi * kBlock + 4 * j) * kSpChunks),
-                                  slot * kTileRowBytes + v_swz(key, pchunk) * 16);
+        const int pchunk = lane % kSpChunks;
+        const int row0 = bi * kBlock + L::kKeysPerLoad * j;
+        buffer_to_lds16_untracked(krs, lds_addr(kdst + row0 * kSpChunks),
+                                  slot * L::kRowBytes + L::kswz(key, pchunk) * 16);
+        buffer_to_lds16_untracked(vrs, lds_addr(vdst + row0 * kSpChunks),
+                                  slot * L::kRowBytes + L::vswz(key, pchunk) * 16);
       }
     }
   };
@@ -138,7 +144,8 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
       const int key = col;
       uint4 a[kD / 16];
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) a[ks] = kbuf[key * kSpChunks + k_swz(key, ks * 2 + half)];
+      for (int ks = 0; ks < kD / 16; ++ks)
+        a[ks] = kbuf[key * kSpChunks + L::kswz(key, ks * 2 + half)];
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks)
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[ks]), as_bf16x8(qreg[ks]),
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
         for (int sub = 0; sub < 2; ++sub) {
           const int key = 16 * s + 8 * sub + 4 * half + jj / 4;
           const char* rowp = reinterpret_cast<const char*>(vbuf + key * kSpChunks);
-          part[sub] = lds_read_tr16(rowp + v_swz(key, unit >> 1) * 16 + (unit & 1) * 8);
+          part[sub] = lds_read_tr16(rowp + L::vswz(key, unit >> 1) * 16 + (unit & 1) * 8);
         }
         a[dt] = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
       }
@@ -208,21 +215,21 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
   };
 
   // Double buffer: tile t in buffer t % 2.  After tile t is consumed, tile t+2 is requested
-  // into its buffer; the counted wait (16 loads per tile) lets exactly that request stay in
-  // flight, and the LDS wait before a reload makes the tile's reads complete first.
+  // into its buffer; the counted wait (kTileLoads loads per tile) lets exactly that request
+  // stay in flight, and the LDS wait before a reload makes the tile's reads complete first.
   load_tile(0, sK0, sV0);
   load_tile(1, sK1, sV1);
-  wait_vmcnt_fence<16>();
+  wait_vmcnt_fence<kTileLoads>();
   for (int t = 0; t < num_tiles; t += 2) {
     compute(t, sK0, sV0);
     lgkm_fence();
     load_tile(t + 2, sK0, sV0);
-    wait_vmcnt_fence<16>();
+    wait_vmcnt_fence<kTileLoads>();
     if (t + 1 >= num_tiles) break;
     compute(t + 1, sK1, sV1);
     lgkm_fence();
     load_tile(t + 3, sK1, sV1);
-    wait_vmcnt_fence<16>();
+    wait_vmcnt_fence<kTileLoads>();
   }
   wait_vmcnt_fence<0>();     // no load may still be writing LDS when the wave ends
 
@@ -247,10 +254,10 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
   }
 }
 
-template <int G>
-static hipError_t launch_shared_g(const SharedPrefixArgs& a) {
+template <int G, int D>
+static hipError_t launch_shared_gd(const SharedPrefixArgs& a) {
   const dim3 grid(a.num_groups * a.row_tiles * a.num_kv_heads, a.nsplit_shared);
-  hipLaunchKernelGGL((pa_shared_prefix_kernel<G>), grid, dim3(kWave), 0, a.stream, a.ws_ml,
+  hipLaunchKernelGGL((pa_shared_prefix_kernel<G, D>), grid, dim3(kWave), 0, a.stream, a.ws_ml,
                      a.ws_acc, static_cast<const bf16_t*>(a.q),
                      static_cast<const bf16_t*>(a.k_cache), static_cast<const bf16_t*>(a.v_cache),
                      a.block_tables, a.group_start, a.shared_blocks, a.seq_lens, a.num_seqs,
@@ -258,6 +265,16 @@ static hipError_t launch_shared_g(const SharedPrefixArgs& a) {
                      a.max_blocks_per_seq, a.row_tiles, a.split_keys, a.slot_base, a.nsplit_max,
                      a.scale_log2);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_shared_g(const SharedPrefixArgs& a) {
+  switch (a.head_dim) {
+    case 64: return launch_shared_gd<G, 64>(a);
+    case 128: return launch_shared_gd<G, 128>(a);
+    case 256: return launch_shared_gd<G, 256>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_shared_prefix(const SharedPrefixArgs& a) {

@@ -9,50 +9,29 @@ namespace pa {
 
 namespace {
 
-constexpr int kD = kTileD;
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;
-constexpr int kTileRows = kWaves * kRowsPerWave;   // 256
-constexpr int kKvTile = 64;                         // keys per LDS tile (4 blocks)
-constexpr int kChunks = kTileChunks;
-constexpr int kRowBytes = kTileRowBytes;
 constexpr int kRankCap = 128;                       // chunks ranked longest-first in-kernel
 constexpr float kLazyLog2 = 8.f;                    // rescale only past 2^8 growth
 
 }  // namespace
 
-// The work-item shape for head_dim D (the constants above are D = 128's).  D 64 and 128: eight
-// waves of 32 rows, 64-key tiles.  D 256: its fp32 accumulators (128 per lane) and Q operand do
-// not fit two waves per SIMD, so four waves of 32 rows (one per SIMD) and 32-key tiles, which
-// keep the 4-stage ring at 128 KiB.  In every shape half the waves stage K and half V, one
-// 16-token block each per tile.
+// The work-item shape for head_dim D.  D 64 and 128: eight waves of 32 rows, 64-key tiles.
+// D 256: its fp32 accumulators (128 per lane) and Q operand do not fit two waves per SIMD, so
+// four waves of 32 rows (one per SIMD) and 32-key tiles, which keep the 4-stage ring at
+// 128 KiB.  In every shape half the waves stage K and half V, one 16-token block each per tile.
 template <int D>
-struct PfShape {
+struct PfShape : KvTile<D> {
+  using L = KvTile<D>;
   static constexpr int kD = D;
-  static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
-  static constexpr int kRowBytes = D * 2;
   static constexpr int kWaves = D == 256 ? 4 : 8;
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kTileRows = kWaves * kRowsPerWave;
   static constexpr int kKvTile = D == 256 ? 32 : 64;      // keys per LDS tile
   static constexpr int kKeySub = kKvTile / 32;           // 32-key score tiles per LDS tile
   static constexpr int kPvSteps = kKvTile / 16;          // 16-key P.V products per d tile
-  static constexpr int kLoads = kBlock * D * 2 / 1024;   // 1 KiB loads per staged block
-  static constexpr int kKeysPerLoad = kWave / kChunks;
-  static constexpr int kRing = kKvTile * kChunks;        // uint4 per K or V ring stage
-  static constexpr int kChunkBits = kChunks == 8 ? 3 : kChunks == 16 ? 4 : 5;
-  static_assert(D == 64 || D == 128 || D == 256, "head_dim");
+  static constexpr int kLoads = L::kLoadsPerBlock;       // 1 KiB loads per staged block
+  static constexpr int kRing = kKvTile * L::kChunks;     // uint4 per K or V ring stage
   static_assert(kWaves / 2 == kKvTile / kBlock, "one wave stages each K and each V block");
-  // Swizzles of the row-major tiles (16-byte chunks of a key row): K rows are read one chunk per
-  // lane down 32 keys, V rows four keys at a time by the transposing load.  For D = 128 these
-  // are k_swz and v_swz.
-  static __device__ __forceinline__ int kswz(int key, int chunk) {
-    return chunk ^ (key & (kChunks - 1));
-  }
-  static __device__ __forceinline__ int vswz(int key, int chunk) {
-    return chunk ^ ((key & 3) << (kChunkBits - 2));
-  }
 };
 
 // Longest-first order of up to kRankCap chunks, kept in LDS: chunk c's items occupy
@@ -68,7 +47,7 @@ struct PrefillRank {
 
 // Every thread of the workgroup calls this (it synchronises); num_chunks <= kRankCap, and the
 // workgroup has at least kRankCap threads.
-template <int G, int TileRows = kTileRows>
+template <int G, int TileRows>
 __device__ __forceinline__ void prefill_rank(PrefillRank& rk, const int32_t* __restrict__ seq_lens,
                                              const int32_t* __restrict__ query_start_loc,
                                              int num_chunks, int num_kv_heads) {
@@ -104,7 +83,7 @@ __device__ __forceinline__ void prefill_rank(PrefillRank& rk, const int32_t* __r
 
 // Item w of the longest-first order as (chunk, row tile, kv head); false past the last item.
 // Every thread of the workgroup calls this (it synchronises).
-template <int G, int TileRows = kTileRows>
+template <int G, int TileRows>
 __device__ __forceinline__ bool prefill_locate(PrefillRank& rk, int w,
                                                const int32_t* __restrict__ query_start_loc,
                                                int num_chunks, int num_kv_heads, int& c,
@@ -130,7 +109,7 @@ __device__ __forceinline__ bool prefill_locate(PrefillRank& rk, int w,
 
 // One work item (chunk c, row tile, kv head) with all PfShape<D>::kThreads threads of the
 // workgroup; the eight arrays are the 4-stage K/V ring, each kKvTile x kChunks 16-byte chunks.
-template <int G, int D = kTileD>
+template <int G, int D>
 __device__ __forceinline__ void prefill_item(
     bf16_t* __restrict__ out, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,

@@ -366,6 +366,21 @@ def test_decode_grouped_matches_oracle(G):
     assert_close(widen(out), oracle_decode(b), ATOL, RTOL, f"grouped G{G}")
 
 
+@pytest.mark.parametrize("D,G", [(64, 1), (64, 4), (256, 2), (256, 4), (256, 8)])
+def test_decode_grouped_head_dims(D, G):
+    """The grouped decode at head_dim 64 (4 KiB key tiles) and 256 (16 KiB tiles, 32 loads per
+    tile in flight) against the oracle, and equal to the plain decode when nothing is shared."""
+    say(f"case: grouped decode, 6 groups, head_dim {D}, G={G}")
+    b = W.make_grouped_decode(GROUPS, 2 * G, 2, D, seed=1800 + G + D, device=DEV)
+    out = grouped(b)
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, f"grouped D{D} G{G}")
+    s = W.make_decode([1, 17, 300, 513, 2049], 2 * G, 2, D, "bf16", seed=1850 + G + D,
+                      device=DEV)
+    S = s.num_seqs
+    alone = run_decode_grouped(s, np.arange(S + 1, dtype=np.int32), np.zeros(S, np.int32), 1)
+    assert torch.equal(alone, run_decode(s))
+
+
 def test_decode_grouped_deterministic_with_dirty_workspace():
     """Two calls, the second with a workspace full of garbage, give the same bits; a larger
     declared max_seq_len (more split slots per row) gives the same bits too."""
