@@ -46,8 +46,8 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 # is reported as null.
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_341_amd", "csrc", f)
                for f in ("pa_decode.hip", "decode_item.hpp")]
-MEASURED_TRAFFIC = {"sha256_prefix": "5e2c59c43a49c0f1",
-                    "split": {"fetch_kib": 243523.2, "write_kib": 4076.0},
+MEASURED_TRAFFIC = {"sha256_prefix": "48f077bcf360726b",
+                    "split": {"fetch_kib": 243523.2, "write_kib": 4075.9},
                     "merge": {"fetch_kib": 2012.8, "write_kib": 336.0},
                     "fetch_scale": 2.0, "write_scale": 1.0}
 

@@ -161,7 +161,9 @@ __device__ __forceinline__ void store_out(bf16_t* p, float v) {
 }
 
 // One split of one (sequence, kv head): `Waves` waves of the calling workgroup share it, and
-// every one of them must make the call (it synchronises the workgroup).  `smem` holds
+// every one of them must make the call (it synchronises the workgroup).  B is the split walk's
+// unit in tokens (the pool's block size for 8- and 16-token blocks; `Rows` maps a unit to its
+// rows), and "block" in the body means such a unit.  `smem` holds
 // max(plan.max_units() * B * G, Waves * G * D) floats (scores, then the waves' partial outputs), `red`
 // Waves x G floats, `stat_m` and `stat_l` G floats each.
 // `Batch` blocks per wave are loaded together before their math (0: 64 tokens' worth).
@@ -180,7 +182,6 @@ __device__ __forceinline__ void decode_split_item(
   constexpr int kBlock = B;
   constexpr int kDecodeBatch = Batch > 0 ? Batch : S::kBatch;
   constexpr int kEpc = S::kEpc;
-  constexpr int kCpr = S::kCpr;
   constexpr int kThreadsW = Waves * kWave;
   const T tag{};
   float* logits = smem;                                  // [split tokens][G]

@@ -1,7 +1,8 @@
 // Paged decode attention for gfx950.
 //
 // Operation: one query token per sequence attends to all of that sequence's cached tokens,
-// which are gathered through its block table from 16-token blocks anywhere in the pool
+// which are gathered through its block table from blocks (16 tokens unless the caller picks
+// another size) anywhere in the pool
 // (cloudmash "Batching and PagedAttention", section "PagedAttention", step 4; study-docs
 // "PagedAttention & Continuous Batching", section "Block tables").  Query head h reads kv head
 // h / G, G = Hq / Hkv, so the G query heads of one kv head share every K/V byte read.
@@ -9,11 +10,12 @@
 // Work split (our design, not from the pages): one workgroup of 4 waves per
 // (sequence, kv head, split), a split being a run of consecutive logical blocks (its length
 // set by the host's split plan, which may shrink toward the later splits).  Inside a split:
-//   phase 1  each wave takes every 4th block, reads its K slab (16 x D contiguous elements),
+//   phase 1  each wave takes every 4th unit of the split (a block of 8 or 16 tokens, a
+//            16-token run of a larger block, or 16 tokens of smaller blocks), reads its K rows,
 //            computes the G scores of every token with lanes split over the head dimension
 //            (DPP sums), and parks them in LDS;
 //   phase 2  exact softmax statistics of the split: max and sum of exp2 per query head;
-//   phase 3  each wave reads the V slabs of the same blocks and accumulates p * V in fp32,
+//   phase 3  each wave reads the V rows of the same units and accumulates p * V in fp32,
 //            lanes split over the head dimension again; waves are summed through LDS.
 // Wave priorities: on a CU the oldest waves win instruction issue, so workgroups dispatched
 // late (onto slots freed by finished splits) were starved by older ones and ended the kernel
