@@ -515,9 +515,11 @@ namespace {
 constexpr size_t kMixedHeader = 256;     // work counters
 constexpr int kMixedMaxChunks = 128;
 constexpr int kMixedMaxSeqs = 2048;
+constexpr int kMixedMaxSplits = 2047;    // split slots per decode sequence
 
 struct MixedPlan {
-  int bps, nsplit;
+  pa::SplitPlan plan;
+  int nsplit;
   size_t ml_bytes, total;
 };
 
@@ -525,15 +527,15 @@ MixedPlan plan_mixed(int num_seqs, int num_q_heads, int num_kv_heads, int head_d
                      int block_size, int dec_max_seq_len) {
   MixedPlan p{};
   if (num_seqs <= 0) {
-    p.bps = 1;
+    p.plan = pa::SplitPlan::uniform(1);
     p.nsplit = 1;
     p.total = kMixedHeader;
     return p;
   }
+  // the standalone decode's plan, so the decode splits shrink toward the last-dispatched ones
   const int g = num_q_heads / num_kv_heads;
-  p.bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, dec_max_seq_len);
-  const int nblk = (dec_max_seq_len + block_size - 1) / block_size;
-  p.nsplit = (nblk + p.bps - 1) / p.bps;
+  p.plan = plan_decode_splits(num_seqs, num_kv_heads, g, block_size, dec_max_seq_len);
+  p.nsplit = p.plan.count((dec_max_seq_len + block_size - 1) / block_size);
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.nsplit;
   p.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
   p.total = kMixedHeader + (p.nsplit > 1 ? p.ml_bytes + rows * head_dim * sizeof(float) : 0);
@@ -605,6 +607,9 @@ pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspa
                 "and %d)", b->num_chunks, b->num_seqs, kMixedMaxChunks, kMixedMaxSeqs);
   const MixedPlan p = plan_mixed(b->num_seqs, b->num_q_heads, b->num_kv_heads, b->head_dim,
                                  b->block_size, b->dec_max_seq_len);
+  if (p.nsplit > kMixedMaxSplits)
+    return fail(PA_ERR_UNSUPPORTED, "pa_mixed_step: %d decode splits per sequence (at most %d)",
+                p.nsplit, kMixedMaxSplits);
   if (!workspace || workspace_bytes < p.total)
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "pa_mixed_step: workspace %zu bytes, need %zu",
                 workspace_bytes, p.total);
@@ -673,7 +678,7 @@ pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspa
   m.dec_seq_lens = b->dec_seq_lens;
   m.num_seqs = b->num_seqs;
   m.dec_max_blocks_per_seq = b->dec_max_blocks_per_seq;
-  m.bps = p.bps;
+  m.plan = p.plan;
   m.nsplit_max = p.nsplit;
   m.ws_ml = ws_ml;
   m.ws_acc = ws_acc;
@@ -701,7 +706,7 @@ pa_status pa_mixed_step(const pa_mixed_batch* b, void* workspace, size_t workspa
   d.num_kv_heads = b->num_kv_heads;
   d.head_dim = b->head_dim;
   d.block_size = b->block_size;
-  d.plan = pa::SplitPlan::uniform(p.bps);
+  d.plan = p.plan;
   d.nsplit_max = p.nsplit;
   d.nsplit_tail = p.nsplit;
   d.skip_blocks = nullptr;

@@ -107,7 +107,9 @@ struct MixedArgs {
   const void* dec_q;
   const int32_t* dec_tables;
   const int32_t* dec_seq_lens;
-  int num_seqs, dec_max_blocks_per_seq, bps, nsplit_max;
+  int num_seqs, dec_max_blocks_per_seq;
+  SplitPlan plan;                // the decode splits, as pa_decode's plan
+  int nsplit_max;
   float* ws_ml;
   float* ws_acc;
   int* queues;                   // two work counters, zero when the kernel starts

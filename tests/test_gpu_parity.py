@@ -708,6 +708,27 @@ def test_mixed_step_single_launch_head_dims(D, G):
     assert_close(widen(dout), want, ATOL, RTOL, f"mixed decodes D{D}")
 
 
+def test_mixed_step_single_launch_long_decodes():
+    """Two 100,000-token decodes beside two chunks: 391 decode splits per sequence (more than
+    the in-kernel split-index tables would hold at one entry per thread), every row against
+    the oracle."""
+    say("case: mixed step single launch, two 100k-token decodes")
+    m = W.mixed_bf16(device=DEV, seed=2200, num_chunks=2, chunk_lens=[40, 300],
+                     prefixes=[10, 900], num_decode=2, median=100000.0, sigma=0.0, cap=131072,
+                     num_q_heads=8, num_kv_heads=2)
+    assert m.decode_seq_lens.tolist() == [100000, 100000]
+    n = ops.pa_mixed_workspace_size(2, 8, 2, 128, 16, 100000)
+    assert n > 2 * 8 * 300 * 130 * 4, "expected hundreds of split slots per row"
+    cout, dout = run_mixed_step(m)
+    kc, vc = raw(m.k_cache), raw(m.v_cache)
+    want = ref.prefill_ref(raw(m.q_chunk), kc, vc, m.chunk_tables, m.chunk_seq_lens,
+                           m.query_start_loc, m.scale, "bf16")
+    assert_close(widen(cout), want, ATOL, RTOL, "mixed chunks beside long decodes")
+    want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, "mixed 100k-token decodes")
+
+
 def test_mixed_step_single_launch_full_size():
     """The full mixed iteration (8 x 512-row chunks, 192 decodes) in one pa_mixed_step call,
     twice with the same garbage-filled workspace (the counters are reset by the call): pool
