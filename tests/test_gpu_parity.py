@@ -729,6 +729,27 @@ def test_mixed_step_single_launch_long_decodes():
     assert_close(widen(dout), want, ATOL, RTOL, "mixed 100k-token decodes")
 
 
+def test_mixed_step_single_launch_tied_lengths():
+    """300 decodes of one length (every sequence ties on its split count) under the shrinking
+    split plan: every workgroup must derive the same decode order, or items are repeated and
+    others skipped; every row against the oracle, and two calls give the same bits."""
+    say("case: mixed step single launch, 300 equal-length decodes")
+    m = W.mixed_bf16(device=DEV, seed=2300, num_chunks=1, chunk_lens=[64], prefixes=[100],
+                     num_decode=300, median=2000.0, sigma=0.0, cap=4096, num_q_heads=8,
+                     num_kv_heads=2)
+    assert set(m.decode_seq_lens.tolist()) == {2000}
+    n = ops.pa_mixed_workspace_size(300, 8, 2, 128, 16, 2000)
+    ws = torch.full((n,), 0x7F, dtype=torch.uint8, device=DEV)     # NaN partials if skipped
+    cout, dout = run_mixed_step(m, workspace=ws)
+    kc, vc = raw(m.k_cache), raw(m.v_cache)
+    want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, "mixed tied decodes")
+    del kc, vc, want
+    cout2, dout2 = run_mixed_step(m, workspace=ws)      # appends the same bytes again
+    assert torch.equal(dout2, dout) and torch.equal(cout2, cout)
+
+
 def test_mixed_step_single_launch_full_size():
     """The full mixed iteration (8 x 512-row chunks, 192 decodes) in one pa_mixed_step call,
     twice with the same garbage-filled workspace (the counters are reset by the call): pool
