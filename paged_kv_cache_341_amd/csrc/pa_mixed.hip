@@ -10,15 +10,17 @@
 // leaves the other's unit idle; here they share the chip at the same time.
 //
 // Design (ours): one workgroup per CU in the prefill item's shape for the head dim (8 waves and
-// 256 rows at head_dim 64 and 128, 4 waves and 128 rows at 256; the 4-stage K/V ring in LDS).  Two work queues, each an atomic counter in the workspace that the
-// append launch before this one zeroes:
+// 256 rows at head_dim 64 and 128, 4 waves and 128 rows at 256; the 4-stage K/V ring in LDS).
+// Two work queues, each an atomic counter in the workspace that the append launch before this
+// one zeroes:
 //   * prefill items (chunk, row tile, kv head), longest chunk first (ranked in LDS from
 //     seq_lens, as in the prefill kernel);
 //   * decode items (split index, sequence, kv head), only the splits that exist, with the
 //     standalone decode's split plan (sizes shrinking toward the later splits): every workgroup
-//     sorts the sequences by split count in LDS (a counting sort), so the sequences that have a
-//     split of index j are a prefix of that order, and the queue hands out every sequence's
-//     first split, then every second split, and so on, the smallest pieces last.
+//     sorts the sequences by split count in LDS, ties by index so that every workgroup gets the
+//     same order, and the sequences that have a split of index j are then a prefix of it; the
+//     queue hands out every sequence's first split, then every second split, and so on, the
+//     smallest pieces last.
 // Workgroups in alternating groups of eight prefer one queue or the other (workgroups reach
 // the 8 XCDs round-robin, so each XCD runs both kinds), and take from the other queue once
 // their own is empty; a workgroup leaves when both are.  Decode splits with more than one
