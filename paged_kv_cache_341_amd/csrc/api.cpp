@@ -353,12 +353,28 @@ pa_status pa_decode_contiguous(void* out, const void* q, const void* k, const vo
 // ------------------------------------------------------------------------- grouped decode
 namespace {
 
-constexpr int kSharedSplitKeys = 512;   // shared keys per shared-prefix work item
-// the shared-prefix kernel keeps a split's block ids one per lane and loads 32 keys per tile
-static_assert(kSharedSplitKeys % 32 == 0 && kSharedSplitKeys <= 64 * 16, "shared split size");
+// Largest number of shared keys one shared-prefix work item takes: the kernel keeps a split's
+// block ids one per lane (at most 64 blocks).
+constexpr int kSharedSplitMax = 64 * 16;
+constexpr int kSharedSplitMin = 64;
+constexpr int64_t kComputeUnits = 256;
+
+// Shared keys per split.  Fewer, longer splits mean fewer partials to write and merge (on 16
+// prompts x 8 beams over 4096 shared tokens, 1024-key splits take 68 us per grouped call warm
+// against 73 us at 512 keys), so splits are as long as possible while the shared-prefix launch
+// still has at least one work item per compute unit.  Its work items are (row tile of 32 rows,
+// kv head, split); num_seqs x G / 32 row tiles per kv head is the fewest the groups can have,
+// and max_seq_len bounds the shared length, so the estimate is a lower bound on the items.
+int plan_shared_split_keys(int num_seqs, int g, int num_kv_heads, int max_seq_len) {
+  const int64_t tiles = (static_cast<int64_t>(num_seqs) * g + 31) / 32 * num_kv_heads;
+  int keys = kSharedSplitMax;
+  while (keys > kSharedSplitMin && tiles * ((max_seq_len + keys - 1) / keys) < kComputeUnits)
+    keys /= 2;
+  return keys;
+}
 
 struct GroupedPlan {
-  int bps, nsplit_shared, nsplit_tail, nsplit_max;
+  int bps, shared_split_keys, nsplit_shared, nsplit_tail, nsplit_max;
   size_t ml_bytes, total;
 };
 
@@ -369,7 +385,8 @@ GroupedPlan plan_grouped(int num_seqs, int num_q_heads, int num_kv_heads, int he
   p.bps = plan_blocks_per_split(num_seqs, num_kv_heads, g, block_size, max_seq_len);
   const int nblk = (max_seq_len + block_size - 1) / block_size;
   p.nsplit_tail = (nblk + p.bps - 1) / p.bps;
-  p.nsplit_shared = (max_seq_len + kSharedSplitKeys - 1) / kSharedSplitKeys;
+  p.shared_split_keys = plan_shared_split_keys(num_seqs, g, num_kv_heads, max_seq_len);
+  p.nsplit_shared = (max_seq_len + p.shared_split_keys - 1) / p.shared_split_keys;
   p.nsplit_max = p.nsplit_shared + p.nsplit_tail;
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * p.nsplit_max;
   p.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
@@ -472,7 +489,7 @@ pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const
   sp.max_blocks_per_seq = max_blocks_per_seq;
   sp.row_tiles = row_tiles;
   sp.nsplit_shared = p.nsplit_shared;
-  sp.split_keys = kSharedSplitKeys;
+  sp.split_keys = p.shared_split_keys;
   sp.slot_base = p.nsplit_shared;
   sp.nsplit_max = p.nsplit_max;
   sp.scale_log2 = scale_log2;
@@ -500,7 +517,7 @@ pa_status pa_decode_grouped(void* out, const void* q, const void* k_cache, const
   a.nsplit_tail = p.nsplit_tail;
   a.skip_blocks = shared_blocks;
   a.slot_base = p.nsplit_shared;
-  a.shared_split_keys = kSharedSplitKeys;
+  a.shared_split_keys = p.shared_split_keys;
   a.scale_log2 = scale_log2;
   a.bf16 = true;
   a.stream = st;

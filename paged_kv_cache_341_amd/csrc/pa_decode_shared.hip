@@ -10,8 +10,10 @@
 // = 32 -- attend to them together.  With 32 rows sharing every key this is a dense
 // contraction, so it runs on MFMA (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 //
-// Design (ours): one wave per work item (group, row tile of 32 rows, kv head, split of
-// `split_keys` shared keys).  Keys stream through LDS 32 at a time, double-buffered, with
+// Design (ours): one wave per work item (group, row tile of 32 rows, kv head, split of the
+// shared keys).  A group's shared blocks are cut into ceil(shared / split_keys) splits as equal
+// as whole blocks allow; the host picks split_keys (at most 64 blocks) as large as keeps one
+// work item per compute unit.  Keys stream through LDS 32 at a time, double-buffered, with
 // buffer-to-LDS loads (16 per tile, always issued, zeros past the split's end) so a counted
 // wait keeps the next tile in flight.  Scores are computed transposed (S^T = K Q^T) so each
 // lane holds one query row; P is rounded to bf16 for the P.V product, read through the
@@ -60,10 +62,14 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
   if (tile * kSpRows >= ng * G) return;
   const int shared_keys =
       min(max(shared_blocks[g0], 0), seq_lens[g0] / kBlock) * kBlock;   // whole blocks only
-  const int k_begin = split * split_keys;
-  if (k_begin >= shared_keys) return;
-  const int k_end = min(shared_keys, k_begin + split_keys);
+  // ns = ceil(shared_keys / split_keys) splits, as the merge counts them, each of whole blocks
+  // and as equal as blocks allow: floor or ceil of nb / ns blocks, so none is empty and none
+  // is longer than split_keys
   const int ns = (shared_keys + split_keys - 1) / split_keys;
+  if (split >= ns) return;
+  const int64_t nb = shared_keys / kBlock;
+  const int k_begin = static_cast<int>(split * nb / ns) * kBlock;
+  const int k_end = static_cast<int>((split + 1) * nb / ns) * kBlock;
   const int num_tiles = (k_end - k_begin + kSpKeys - 1) / kSpKeys;
   // the shared blocks have the same ids in every member's table: read the first member's
   const int32_t* table = block_tables + static_cast<size_t>(g0) * max_blocks_per_seq;

@@ -151,10 +151,30 @@ def test_grouped_decode_rejects(kw, status):
     assert ops.load_library().pa_last_error().decode().startswith("pa_decode_grouped")
 
 
+def _shared_split_keys(num_seqs, g, num_kv_heads, max_seq_len):
+    # the library's rule: the longest split (at most 64 blocks, at least 64 keys) that leaves
+    # the shared-prefix launch at least 256 work items (row tiles x kv heads x splits)
+    tiles = -(-num_seqs * g // 32) * num_kv_heads
+    keys = 1024
+    while keys > 64 and tiles * -(-max_seq_len // keys) < 256:
+        keys //= 2
+    return keys
+
+
 def test_grouped_workspace_size():
-    n = ops.pa_decode_grouped_workspace_size(128, 32, 8, 128, 16, 4400)
-    # every row holds its shared-prefix splits and its own splits
-    assert n >= 128 * 32 * (4400 // 512 + 1) * (128 + 2) * 4
+    # every row holds its shared-prefix splits and at least one own split
+    for S, L in [(128, 4400), (2, 4400), (40, 9000), (1, 100), (512, 70000)]:
+        ns = -(-L // _shared_split_keys(S, 4, 8, L))
+        n = ops.pa_decode_grouped_workspace_size(S, 32, 8, 128, 16, L)
+        assert n >= S * 32 * (ns + 1) * (128 + 2) * 4, (S, L)
+    assert _shared_split_keys(128, 4, 8, 4400) == 1024      # 16 prompts x 8 beams
+    assert _shared_split_keys(2, 4, 8, 4400) == 128
+    assert _shared_split_keys(1, 4, 8, 100) == 64
+    # slots per row: the shared ones plus the own ones, at most one own split per 16 blocks
+    S, L = 128, 4400
+    n = ops.pa_decode_grouped_workspace_size(S, 32, 8, 128, 16, L)
+    slots = n // (S * 32 * (128 + 2) * 4)
+    assert -(-L // 1024) + 1 <= slots <= -(-L // 1024) + -(-L // 256), slots
     assert ops.pa_decode_grouped_workspace_size(128, 32, 8, 128, 32, 4400) == 0
     assert ops.pa_decode_grouped_workspace_size(4, 6, 4, 128, 16, 100) == 0
 

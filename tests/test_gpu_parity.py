@@ -344,8 +344,10 @@ def test_decode_merge_ignores_unused_workspace_slots():
 
 
 # ------------------------------------------------------------------------------ grouped decode
-# (prefix, [tail per member]) per group: 8 forks over three shared splits (512, 512, 176 keys)
-# with a copied partial block; a single sequence; 3 identical forks whose every block is
+# (prefix, [tail per member]) per group: 8 forks over a 1200-token prefix with a copied partial
+# block (so few rows that the prefix is cut into the shortest splits, 64 keys: 19 splits of 3 or
+# 4 blocks, and every row merges more partials than one round trip takes); a single sequence;
+# 3 identical forks whose every block is
 # shared (no own blocks left); 4 forks that share no full block; 2 forks sharing one block;
 # 5 forks over 2057 tokens (5 x G rows: two row tiles at G = 8).
 GROUPS = [(1200, [5, 1, 16, 33, 100, 0, 2, 700]), (300, [20]), (640, [0, 0, 0]),
@@ -379,6 +381,23 @@ def test_decode_grouped_head_dims(D, G):
     S = s.num_seqs
     alone = run_decode_grouped(s, np.arange(S + 1, dtype=np.int32), np.zeros(S, np.int32), 1)
     assert torch.equal(alone, run_decode(s))
+
+
+# 4 groups of 8 forks over prefixes up to 4100 tokens plus 32 single sequences, 32/8 heads:
+# enough rows that the shared prefixes are cut into the longest splits (64 blocks of 16 keys;
+# the 4096-token prefix into four such splits, the 2500-token one into three of 52 blocks)
+LONG_GROUPS = ([(4100, [3, 10, 100, 1, 256, 17, 64, 33]), (2500, [5, 1, 16, 33, 100, 0, 2, 70]),
+                (3000, [9, 9, 9, 9, 9, 9, 9, 9]), (1030, [1, 2, 3, 4, 5, 6, 7, 8])]
+               + [(40 + 37 * i, [1 + i]) for i in range(32)])
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_decode_grouped_longest_shared_splits(D):
+    say(f"case: grouped decode, 64 sequences over 4100-token prefixes, head_dim {D}")
+    b = W.make_grouped_decode(LONG_GROUPS, 32, 8, D, seed=1900 + D, device=DEV)
+    assert b.num_seqs == 64 and b.max_seq_len >= 4100
+    out = grouped(b)
+    assert_close(widen(out), oracle_decode(b), ATOL, RTOL, f"grouped long splits D{D}")
 
 
 def test_decode_grouped_deterministic_with_dirty_workspace():
