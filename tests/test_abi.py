@@ -231,6 +231,64 @@ def test_mixed_batch_layout(tmp_path):
     assert ops.pa_mixed_workspace_size(8, 16, 4, 96, 16, 4096) == 0
 
 
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "pagedattn.h"
+#include "block_manager.h"
+int main(void) {
+  size_t ws = pa_decode_workspace_size(64, 32, 8, 128, 16, 4096);
+  if (ws == 0) return 1;
+  if (pa_decode_workspace_size(64, 32, 8, 128, 7, 4096) != 0) return 2;
+  pa_status s = pa_decode(NULL, NULL, NULL, NULL, NULL, NULL, 64, 32, 8, 128, 16, 1000, 256,
+                          4096, 0.088f, PA_DTYPE_BF16, NULL, 0, NULL);
+  if (s != PA_ERR_INVALID_ARGUMENT) return 3;
+  if (strncmp(pa_last_error(), "pa_decode", 9) != 0) return 4;
+  if (strlen(pa_status_string(s)) == 0) return 5;
+  pa_bm* bm = pa_bm_create(8, 0, 16, NULL, NULL);
+  if (!bm) return 6;
+  int64_t slots[64];
+  if (pa_bm_add_sequence(bm, 1, 40, slots) != PA_BM_OK) return 7;
+  if (pa_bm_fork(bm, 1, 2) != PA_BM_OK) return 8;
+  int64_t cow[2];
+  int32_t ncow = 0;
+  if (pa_bm_append(bm, 2, 1, slots, cow, 1, &ncow) != PA_BM_OK || ncow != 1) return 9;
+  int32_t table[4];
+  if (pa_bm_table(bm, 2, table, 4) != PA_BM_OK) return 10;
+  printf("%zu %d %lld %lld %lld %d %d %d\n", ws, (int)s, (long long)cow[0], (long long)cow[1],
+         (long long)slots[0], table[0], table[1], table[2]);
+  pa_bm_destroy(bm);
+  return 0;
+}
+"""
+
+
+def test_c_program_uses_the_library(tmp_path):
+    """The boundary is plain C: a C99 program built against include/*.h and linked with the
+    library gets the same workspace size as the binding, a rejected null argument with its
+    message, and the native block manager's copy-on-write of a forked partial block (a 40-token
+    sequence over blocks 0, 1, 2; its fork appends token 40, which lands in a copy of block 2,
+    block 3, at slot 3 * 16 + 8).  Nothing here touches a GPU."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    lib = ops.load_library()
+    libdir = os.path.dirname(os.path.abspath(lib._name))
+    src = tmp_path / "prog.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "prog"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    f"-I{os.path.join(ROOT, 'include')}", str(src), f"-L{libdir}", "-lpagedattn",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    ws, status, src_blk, dst_blk, slot, *table = (int(x) for x in r.stdout.split())
+    assert ws == ops.pa_decode_workspace_size(64, 32, 8, 128, 16, 4096)
+    assert status == 1                        # PA_ERR_INVALID_ARGUMENT
+    assert (src_blk, dst_blk, slot, table) == (2, 3, 56, [0, 1, 3])
+
+
 def _prefill(**kw):
     a = dict(out=P, q=P, k=P, v=P, bt=P, sl=P, qsl=P, C=8, T=4096, maxq=512, maxlen=8704,
              Hq=32, Hkv=8, D=128, B=16, NB=1000, MB=600, scale=0.1, dtype=1)
