@@ -45,6 +45,22 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A lane's value combined with the one lane l ^ 32 holds (the other half of the wave), through
+// one v_permlane32_swap (gfx950): swapping x with itself leaves {x[l], x[l + 32]} in the lower
+// half and {x[l - 32], x[l]} in the upper one, so the two results hold both values in every
+// lane.  An LDS permute did this before (on the prefill's per-step row max, 1-2% of the kernel).
+// max and + are commutative, so both halves get the same bits.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Raw buffer descriptor over `bytes` bytes at `base`: loads past the end return zeros (and a
 // buffer-to-LDS load writes zeros).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
     float mx = sacc[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_with_other_half(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy_raw) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2((m_run - m_new) * scale_log2);
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kWave) void pa_shared_prefix_kernel(
   }
   wait_vmcnt_fence<0>();     // no load may still be writing LDS when the wave ends
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = add_other_half(l_run);
   if (row_valid) {
     const size_t row = static_cast<size_t>(seq) * Hq + kvh * G + head;
     const size_t slot = row * nsplit_max + (slot_base - ns + split);

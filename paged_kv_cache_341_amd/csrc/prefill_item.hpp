@@ -265,7 +265,7 @@ __device__ __forceinline__ void prefill_item(
       for (int t2 = 0; t2 < Sh::kKeySub; ++t2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, cur[t2][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_with_other_half(mx);
       // raise the running max only when some row of the wave grew past the lazy margin
       if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy_raw) != 0) {
         const float m_new = fmaxf(m_run, mx);
@@ -358,7 +358,7 @@ __device__ __forceinline__ void prefill_item(
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
   // ------------------------------------------------------------------------- write out
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = add_other_half(l_run);
   const float inv = 1.f / l_tot;
   if (row_valid) {
     bf16_t* op = out + (static_cast<size_t>(q0 + t_row) * Hq + kvh * G + (r % G)) * kD;
