@@ -104,3 +104,36 @@ def test_decode_grouped_random_shapes(seed):
     want = ref.decode_ref(raw(b.q), raw(b.k_cache), raw(b.v_cache), b.block_tables, b.seq_lens,
                           b.scale, "bf16", b.block_size)
     assert_close(widen(out), want, ATOL, RTOL, f"random grouped {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mixed_step_random_shapes(seed):
+    """pa_mixed_step (append, chunk tiles and decode splits in one persistent launch, then the
+    merge) on drawn chunks and a drawn number of lognormal decodes: the pool bit-exact against
+    the oracle's append, every chunk row and every decode row against the oracle."""
+    from tests.gpu_util import run_mixed_step
+    rng = np.random.default_rng(7700 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128, 256]))
+    C = int(rng.integers(1, 7))
+    chunk_lens = _lengths(rng, C, 400, 16)
+    prefixes = [int(x) for x in rng.integers(0, 3000, size=C)]
+    Sd = int(rng.integers(1, 301))
+    median = float(rng.choice([30.0, 300.0, 1500.0]))
+    say(f"case: pa_mixed_step seed {seed}: G={G} Hkv={Hkv} D={D} chunks {chunk_lens} over "
+        f"{prefixes}, {Sd} decodes (median {median})")
+    m = W.mixed_bf16(device=DEV, seed=7800 + seed, num_chunks=C, chunk_lens=chunk_lens,
+                     prefixes=prefixes, num_decode=Sd, median=median, cap=6000,
+                     num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D)
+    bk, bv = raw(m.k_cache), raw(m.v_cache)
+    cout, dout = run_mixed_step(m)
+    wk, wv = ref.append_ref(bk, bv, raw(m.k_new), raw(m.v_new), m.slot_mapping)
+    kc, vc = raw(m.k_cache), raw(m.v_cache)
+    assert np.array_equal(kc, wk) and np.array_equal(vc, wv), f"mixed pool {seed}"
+    want = ref.prefill_ref(raw(m.q_chunk), kc, vc, m.chunk_tables, m.chunk_seq_lens,
+                           m.query_start_loc, m.scale, "bf16")
+    assert_close(widen(cout), want, ATOL, RTOL, f"random mixed chunks {seed}")
+    want = ref.decode_ref(raw(m.q_decode), kc, vc, m.decode_tables, m.decode_seq_lens, m.scale,
+                          "bf16")
+    assert_close(widen(dout), want, ATOL, RTOL, f"random mixed decodes {seed}")
