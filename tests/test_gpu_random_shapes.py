@@ -5,8 +5,9 @@ Here each case draws its shape: the number of sequences, lengths spread over 1 t
 thousand tokens with block-edge values (multiples of the block size and one either side)
 mixed in, query heads per kv head, kv heads, head_dim and, for pa_decode, the block size and
 the element type; prefill chunks draw their row counts and prefixes; the grouped decode draws
-its forks (prefix and tails).  The split plans and the shared-prefix partition then see
-shapes nobody chose.  Every unowned pool slot holds NaN, outputs and workspaces sit between
+its forks (prefix and tails); the single-launch mixed step draws chunks beside 1 to 300
+lognormal decodes.  The split plans, the shared-prefix partition and the mixed kernel's work
+queues then see shapes nobody chose.  Every unowned pool slot holds NaN, outputs and workspaces sit between
 canary guards, and tolerances are those of test_gpu_parity.py.
 """
 import numpy as np
