@@ -20,7 +20,10 @@ import hashlib
 import json
 import math
 import os
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -73,6 +76,54 @@ def prewarm(fn, ms: float):
         for _ in range(64):
             fn()
         torch.cuda.synchronize()
+
+
+SPEC_SCLK_MHZ = 2400.0          # the shader clock the dense MFMA peak assumes
+
+
+def gfx_clock_mhz_under_load(fn, max_s: float = 20.0) -> float | None:
+    """Mean GFX clock (MHz) over the XCDs, as amd-smi reports it while fn() runs back to back,
+    or None when amd-smi is missing or its output cannot be read.  Under the matrix-core load of
+    the prefill the chip holds a lower clock than the 2.4 GHz its dense peak assumes; this is
+    the clock to price the prefill's rate against.  Reads the first GPU amd-smi lists (the
+    benchmark runs on one GPU)."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    out = {}
+
+    def sample():
+        try:
+            r = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True, text=True,
+                               timeout=max_s)
+            out["text"] = r.stdout
+        except (OSError, subprocess.SubprocessError):
+            pass
+
+    for _ in range(20):                      # the clock is up before the sample is taken
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.time()
+    while th.is_alive() and time.time() - t0 < max_s:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    return parse_gfx_clock_mhz(out.get("text", ""))
+
+
+def parse_gfx_clock_mhz(text: str) -> float | None:
+    """Mean of the gfx_<i> clocks of the first GPU in `amd-smi metric -c --json` output."""
+    try:
+        data = json.loads(text)
+        gpu = (data["gpu_data"] if isinstance(data, dict) else data)[0]
+        clk = [float(v["clk"]["value"]) for k, v in gpu["clock"].items()
+               if k.startswith("gfx_") and isinstance(v["clk"]["value"], (int, float))]
+        return sum(clk) / len(clk) if clk else None
+    except (ValueError, KeyError, IndexError, TypeError, AttributeError):
+        return None
 
 
 def time_calls(fn, steps: int, warmup: int, prewarm_ms: float | None = None):
@@ -360,6 +411,7 @@ def bench_mixed(steps, warmup, overlap=False):
     cold_pre = time_cold(prefill, max(steps, 20), flush)
     cold_dec = time_cold(dfn, max(steps, 20), flush)
     del flush
+    sclk = gfx_clock_mhz_under_load(prefill)
     T = len(m.slot_mapping)
     flops = chunk_flops(m.extra["prefixes"], np.diff(m.query_start_loc), 32, 128)
     app_bytes = 2 * T * 8 * 128 * 2 * 2          # read + write of K and V rows
@@ -385,7 +437,11 @@ def bench_mixed(steps, warmup, overlap=False):
                           "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                           "achieved_cold": round(tflops_cold, 1),
                           "frac_cold": round(tflops_cold / BF16_PEAK_TFLOPS, 4),
-                          "algorithmic_flops": flops},
+                          "algorithmic_flops": flops,
+                          # the same rate priced at the clock the chip held while it ran
+                          "sclk_mhz": None if sclk is None else round(sclk, 1),
+                          "frac_at_sclk": None if not sclk else
+                          round(tflops / (BF16_PEAK_TFLOPS * sclk / SPEC_SCLK_MHZ), 4)},
         decode_roofline={"bound": "hbm", "kernel": "pa_decode_split_kernel + "
                                                    "pa_decode_merge_kernel",
                          "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -405,6 +461,9 @@ def bench_mixed(steps, warmup, overlap=False):
         f"{res['tokens_per_s_cold']:.0f} tok/s | prefill {cold_pre['median_ms'] * 1e3:.1f} us "
         f"{tflops_cold:.0f} TFLOP/s | decode {cold_dec['median_ms'] * 1e3:.1f} us "
         f"{dec_gbps_cold:.0f} GB/s")
+    if sclk:
+        log(f"prefill under load: GFX clock {sclk:.0f} MHz (amd-smi) -> "
+            f"{100 * res['prefill_roofline']['frac_at_sclk']:.1f}% of the MFMA peak at that clock")
     log(f"mixed step as one pa_mixed_step call (single launch): {t_single[0] * 1e3:.1f} us -> "
         f"{res['single_launch_tokens_per_s']:.0f} tok/s")
     log(f"mixed step replayed from a HIP graph: {t_graph[0] * 1e3:.1f} us -> "

@@ -39,3 +39,24 @@ def test_traffic_is_null_once_the_sources_change(monkeypatch):
     m = dict(bench.MEASURED_TRAFFIC, sha256_prefix="0" * 16)
     monkeypatch.setattr(bench, "MEASURED_TRAFFIC", m)
     assert bench.measured_traffic() is None
+
+
+def test_parse_gfx_clock_mhz():
+    """The amd-smi clock reading: the mean over the XCDs' gfx clocks of the first GPU, None on
+    output it cannot read."""
+    import json
+    import bench
+    def xcd(mhz):
+        return {"clk": {"value": mhz, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                "max_clk": {"value": 2400, "unit": "MHz"}}
+    clocks = {f"gfx_{i}": xcd(2000 + 10 * i) for i in range(8)}
+    clocks["mem_0"] = xcd(1300)                      # not a gfx clock: ignored
+    text = json.dumps({"gpu_data": [{"gpu": 0, "clock": clocks}]})
+    assert bench.parse_gfx_clock_mhz(text) == 2035.0
+    assert bench.parse_gfx_clock_mhz(json.dumps([{"gpu": 0, "clock": clocks}])) == 2035.0
+    clocks["gfx_3"]["clk"]["value"] = "N/A"          # an unreadable XCD drops out
+    assert bench.parse_gfx_clock_mhz(text.replace('"value": 2030', '"value": "N/A"')) == \
+        (sum(2000 + 10 * i for i in range(8)) - 2030) / 7
+    assert bench.parse_gfx_clock_mhz("") is None
+    assert bench.parse_gfx_clock_mhz("amd-smi: error") is None
+    assert bench.parse_gfx_clock_mhz(json.dumps({"gpu_data": []})) is None
